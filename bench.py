@@ -1,0 +1,300 @@
+"""Benchmark of the windowed attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+
+One step = one call of atw_prefill (window planning + the windowed prefill
+kernel) on the Llama-3.2-3B-shaped attention layer at 128K tokens
+(batch 1, 24 query / 8 kv heads, d = 128, rope base 5e5, k = 8, causal, bf16,
+inputs resident in HBM).  ``value`` is the algorithmic throughput of that
+step: (2*d*C + 4*R) flops per (batch, query head), C = visible cells,
+R = retained pair-terms, divided by the measured step time.
+
+Also reported on the same line: the dense-equivalent rate, window ON/OFF
+speedups (128K and the 32K/64K sweep, the Qwen2.5-0.5B 32K shape), the
+split-KV decode HBM rate on the Qwen2.5-7B-1M-shaped 512K cache (8
+sequences, 64 splits), the prefill kernel's roofline fraction from
+per-launch HIP events, and the fp64 CPU oracle timed on a bounded sample.
+Inputs are seeded synthetic N(0,1) tensors (see rope_frequency_pair_amd.synth).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+HEADLINE = "llama-3.2-3b-128k"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_llama128k_traffic.json")
+KERNEL_SOURCES = ["rope_frequency_pair_amd/csrc/prefill.hip", "rope_frequency_pair_amd/csrc/device_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(atw, n, d, h_q, batch, base, k_turns, window_on):
+    """(algorithmic, dense-equivalent) flops of one causal prefill of length n."""
+    pruned, total = atw.pruned_terms(n, n, 0, d, base, k_turns, True, window_on)
+    h = d // 2
+    cells = total // h
+    retained = total - pruned
+    per_head_alg = 2 * d * cells + 4 * retained
+    per_head_dense = 4 * d * cells
+    return per_head_alg * h_q * batch, per_head_dense * h_q * batch, pruned / total
+
+
+def decode_bytes(atw, L, d, h_kv, batch, base, k_turns, window_on):
+    """Algorithmic HBM bytes of one decode step: retained K pair slices
+    (2 bytes per element, exact per-key window) + all of V, per kv head."""
+    pruned, total = atw.pruned_terms(1, L, L, d, base, k_turns, True, window_on)
+    h = d // 2
+    k_bytes = 4 * (total - pruned)      # total pair-terms of the row = h * L; 2 elems * 2 B each
+    v_bytes = 2 * d * L
+    return (k_bytes + v_bytes) * h_kv * batch, pruned / total
+
+
+def time_launches(fn, stream, n):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(sample_rows=96):
+    """Time the fp64 oracle on a bounded sample of the headline workload."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    from rope_frequency_pair_amd import synth
+    w = synth.WORKLOADS[HEADLINE]
+    workers = max(1, min(16, os.cpu_count() or 1, sample_rows))
+    rng = np.random.default_rng(0)
+    rows = sorted(int(x) for x in rng.integers(w.n // 2, w.n, size=sample_rows))
+    # inputs of one (query head, kv head) pair on the CPU generator: same shape,
+    # same distribution as the GPU draw
+    g = synth.generator(w.seed)
+    q = torch.randn((w.n, w.head_dim), generator=g)[rows].to(torch.bfloat16).float().numpy()
+    k = torch.randn((w.n, w.head_dim), generator=g).to(torch.bfloat16).float().numpy()
+    v = torch.randn((w.n, w.head_dim), generator=g).to(torch.bfloat16).float().numpy()
+    chunks = [list(range(i, len(rows), workers)) for i in range(workers)]
+    args = [(q[c], k, v, [rows[i] for i in c], w.rope_base, w.k_turns) for c in chunks if c]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(args)) as pool:
+        pool.map(_oracle_rows, args)
+    dt = time.perf_counter() - t0
+    h = w.head_dim // 2
+    import oracle
+    flops = 0
+    for r in rows:
+        p, t = oracle.pruned_terms(1, r + 1, r, w.head_dim, w.rope_base, w.k_turns)
+        flops += 2 * w.head_dim * (r + 1) + 4 * (t - p)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(args), "kind": "oracle",
+            "sample": f"{len(rows)} query rows (positions {rows[0]}..{rows[-1]}) of one head of the "
+                      f"128K Llama-3.2-3B-shaped prefill, window on, float64 numpy; {dt:.1f} s wall"}
+
+
+def _oracle_rows(a):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    import numpy as np
+    import oracle
+    q, k, v, rows, base, k_turns = a
+    for i, r in enumerate(rows):
+        oracle.prefill(q[None, None, i:i + 1], k[None, None, :r + 1], v[None, None, :r + 1], r, base, k_turns)
+    return len(rows)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=6)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--quick", action="store_true", help="headline prefill only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each call runs on one device; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_frequency_pair_amd as atw
+    from rope_frequency_pair_amd import synth
+
+    atw.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[HEADLINE]
+    log(f"[bench] {atw.version()} on {torch.cuda.get_device_name(0)}; inputs for {w.name}")
+    q, k, v = synth.workload_prefill_inputs(w)
+    out = torch.empty_like(q)
+
+    def step(on=True, qq=q, kk=k, vv=v, oo=out, wl=w):
+        atw.prefill(qq, kk, vv, rope_base=wl.rope_base, k_turns=wl.k_turns, window_on=on, out=oo)
+
+    flops_on, dense, share = prefill_flops(atw, w.n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, True)
+    flops_off, _, _ = prefill_flops(atw, w.n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, False)
+
+    for _ in range(args.warmup):
+        step(True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    launch_ms = time_launches(lambda: step(True), stream, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = statistics.mean(launch_ms)
+    value = flops_on / (ms_step * 1e-3) / 1e12
+
+    # window ON vs OFF, interleaved, median of >= 6 rounds each
+    rounds = max(6, args.steps)
+    on_ms, off_ms = [], []
+    for _ in range(rounds):
+        on_ms += time_launches(lambda: step(True), stream, 1)
+        off_ms += time_launches(lambda: step(False), stream, 1)
+    med_on, med_off = statistics.median(on_ms), statistics.median(off_ms)
+    ceiling = 2.0 / (1.0 + (1.0 - share))
+    result = {
+        "metric": "windowed prefill TFLOP/s (Llama-3.2-3B shape, 128K, window on)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.n, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "head_dim": w.head_dim, "rope_base": w.rope_base, "k": w.k_turns, "causal": True,
+                   "parallelism": "none (1 GPU)"},
+        "prefill_128k": {
+            "pruned_share": round(share, 4),
+            "tflops_algorithmic_on": round(flops_on / (med_on * 1e-3) / 1e12, 1),
+            "tflops_dense_equiv_on": round(dense / (med_on * 1e-3) / 1e12, 1),
+            "tflops_off": round(flops_off / (med_off * 1e-3) / 1e12, 1),
+            "ms_on_median": round(med_on, 3),
+            "ms_off_median": round(med_off, 3),
+            "on_off_speedup": round(med_off / med_on, 3),
+            "ceiling_2_over_1_plus_s": round(ceiling, 3),
+        },
+    }
+    sha = kernel_sha()
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            prof = json.load(f)
+        if prof.get("kernel_sha") == sha:
+            traffic = prof.get("traffic_bytes")
+    result["roofline"] = {"bound": "mfma", "achieved": round(flops_on / (kern_ms * 1e-3) / 1e12, 1),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(flops_on / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "traffic": traffic, "kernel": "prefill_kernel<bf16,128>",
+                          "kernel_ms_mean": round(kern_ms, 3), "kernel_sha": sha}
+
+    if not args.quick:
+        # ON/OFF sweep for "ON beats OFF at every context >= 32K"
+        sweep = {}
+        for n in (32768, 65536):
+            qs, ks, vs = q[:, :, :n], k[:, :, :n], v[:, :, :n]
+            os_ = out[:, :, :n]
+            a, b = [], []
+            for _ in range(6):
+                a += time_launches(lambda: step(True, qs, ks, vs, os_), stream, 1)
+                b += time_launches(lambda: step(False, qs, ks, vs, os_), stream, 1)
+            fo, _, sh = prefill_flops(atw, n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, True)
+            sweep[str(n)] = {"ms_on": round(statistics.median(a), 3), "ms_off": round(statistics.median(b), 3),
+                             "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+                             "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
+                             "pruned_share": round(sh, 4)}
+        result["prefill_llama_sweep"] = sweep
+        del q, k, v, out
+        torch.cuda.empty_cache()
+
+        # Qwen2.5-0.5B shape, 32K, d = 64
+        wq = synth.WORKLOADS["qwen2.5-0.5b-32k"]
+        log(f"[bench] {wq.name}")
+        q1, k1, v1 = synth.workload_prefill_inputs(wq)
+        o1 = torch.empty_like(q1)
+        a, b = [], []
+        for _ in range(6):
+            a += time_launches(lambda: step(True, q1, k1, v1, o1, wq), stream, 1)
+            b += time_launches(lambda: step(False, q1, k1, v1, o1, wq), stream, 1)
+        fo, fd, sh = prefill_flops(atw, wq.n, wq.head_dim, wq.h_q, wq.batch, wq.rope_base, wq.k_turns, True)
+        result["prefill_qwen_32k"] = {"ms_on": round(statistics.median(a), 3),
+                                      "ms_off": round(statistics.median(b), 3),
+                                      "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+                                      "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
+                                      "tflops_dense_equiv_on": round(fd / (statistics.median(a) * 1e-3) / 1e12, 1),
+                                      "pruned_share": round(sh, 4)}
+        del q1, k1, v1, o1
+        torch.cuda.empty_cache()
+
+        # split-KV decode, Qwen2.5-7B-1M shape, 512K cache, 8 sequences, 64 splits
+        wd = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+        log(f"[bench] {wd.name}")
+        qd, kc, vc = synth.workload_decode_inputs(wd)
+        L = wd.n
+        ws = torch.empty(atw.decode_workspace_bytes(wd.batch, wd.h_q, wd.head_dim, wd.splits),
+                         dtype=torch.uint8, device=dev)
+        od = torch.empty((wd.batch, wd.h_q, wd.head_dim), dtype=torch.bfloat16, device=dev)
+
+        def dstep(on):
+            atw.decode(qd, kc, vc, [L] * wd.batch, [L] * wd.batch, rope_base=wd.rope_base,
+                       k_turns=wd.k_turns, window_on=on, num_splits=wd.splits, workspace=ws, out=od)
+
+        for _ in range(3):
+            dstep(True)
+            dstep(False)
+        a, b = [], []
+        for _ in range(10):
+            a += time_launches(lambda: dstep(True), stream, 1)
+            b += time_launches(lambda: dstep(False), stream, 1)
+        by_on, sh = decode_bytes(atw, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base, wd.k_turns, True)
+        by_off, _ = decode_bytes(atw, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base, wd.k_turns, False)
+        ma, mb = statistics.median(a), statistics.median(b)
+        result["decode_512k"] = {"ms_on": round(ma, 4), "ms_off": round(mb, 4),
+                                 "gbs_algorithmic_on": round(by_on / (ma * 1e-3) / 1e9, 1),
+                                 "gbs_off": round(by_off / (mb * 1e-3) / 1e9, 1),
+                                 "hbm_frac_on": round(by_on / (ma * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "hbm_frac_off": round(by_off / (mb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "on_off_speedup": round(mb / ma, 3),
+                                 "k_pair_terms_pruned": round(sh, 4),
+                                 "bytes_on": by_on, "bytes_off": by_off}
+        del qd, kc, vc
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * atw.h -- C ABI of libatw: causal attention with the per-RoPE-wavelength
+ * distance window, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources: "ATFlash — Per-RoPE-Wavelength Attention Windows",
+ * README sections "The idea" and "Porting to something else"; "ATFlash:
+ * Per-RoPE-Wavelength Attention Windows for Compute/Memory-Efficient LLM
+ * Inference", arXiv abstract):
+ *
+ *   head dim d, h = d/2 rotation pairs, pair r = dims (r, r + d/2)
+ *   (rotate-half layout); theta_r = base^(-2r/d); wavelength
+ *   lambda_r = 2*pi/theta_r; window w_r = k * lambda_r.
+ *   RoPE rotates pair r of the query at position n by n*theta_r and of the
+ *   key at position m by m*theta_r, so its term of the score depends only on
+ *   (n - m)*theta_r.  The term of pair r is kept while the query-key distance
+ *   is at most w_r and is zero beyond it; the rest of the sum is kept
+ *   unchanged, and the softmax over keys (running max, normalizer) is the
+ *   ordinary one.  Every key stays visible through the low-frequency pairs.
+ *
+ *   s(n, m) = scale * sum_r [dist(n, m) <= W_r] * (q'_r k'_r + q'_{r+h} k'_{r+h})
+ *   with W_r = floor(w_r), q', k' the rotated vectors, scale = 1/sqrt(d)
+ *   unless given; dist = n - m (causal) or |n - m| (non-causal).
+ *   O_n = sum_m softmax_m(s(n, .)) v_m over the visible keys.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are pre-RoPE; the rotation is applied inside the kernels as the
+ *     data is loaded ("RoPE fused at load").
+ *   - Element strides are given per tensor as int64 element counts; the head
+ *     dimension is contiguous (stride 1).  Base pointers must be 16-byte
+ *     aligned and every stride a multiple of 16 bytes / element size.
+ *   - Every device pointer is allocated and owned by the caller; the library
+ *     allocates no device memory and keeps no state between calls except a
+ *     thread-local error string.  Inputs are never written; outputs are fully
+ *     written.
+ *   - Calls are asynchronous on the given HIP stream (hipStream_t, passed as
+ *     void*; NULL = the default stream).  Execution errors surface when the
+ *     caller synchronizes.  Argument errors are detected before any launch,
+ *     so an error return leaves every output untouched.
+ *   - window_on = 0 is the plain causal RoPE attention path (k is ignored);
+ *     k = +inf with window_on = 1 gives the same result.
+ *   - Supported on the GPU: head_dim 64 or 128; dtype ATW_BF16 (bf16 in and
+ *     out, fp32 accumulation, bf16 MFMA) for prefill and decode, ATW_F32
+ *     (fp32 in and out, fp32 MFMA) for prefill.  Positions must be < 2^31.
+ */
+#ifndef ATW_H
+#define ATW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATW_OK 0
+#define ATW_EINVAL (-1)        /* invalid argument (null pointer, bad size, bad value) */
+#define ATW_EUNSUPPORTED (-2)  /* valid but not supported (head_dim, dtype, alignment) */
+#define ATW_EWORKSPACE (-3)    /* decode workspace missing or too small */
+#define ATW_EHIP (-4)          /* the HIP runtime reported an error at launch */
+
+/* element types */
+#define ATW_F32 0
+#define ATW_BF16 1
+
+/* Largest integer window; returned for every pair when the window is off or
+ * k = +inf (2^62). */
+#define ATW_UNBOUNDED ((int64_t)1 << 62)
+
+/*
+ * atw_prefill -- windowed causal (or non-causal) attention for a block of
+ * queries against a key/value sequence ("The idea": the window is a slice of
+ * the query-key contraction axis; "Porting to something else": the pair loop
+ * starts at the window boundary and the rotation is fused at load).
+ *
+ *   q  [batch, h_q,  n_q,  head_dim]   query i is at position q_pos0 + i
+ *   k  [batch, h_kv, n_kv, head_dim]   key j is at position j
+ *   v  [batch, h_kv, n_kv, head_dim]
+ *   o  [batch, h_q,  n_q,  head_dim]   written
+ *   *_strides[3] = element strides of (batch, head, token).
+ *   kv_head_of_q: host array [h_q] giving the kv head each query head reads
+ *     (grouped-query attention); NULL = h // (h_q / h_kv).
+ *   causal: 1 = key j visible iff j <= query position (a chunked prefill
+ *     passes q_pos0 = tokens already cached and n_kv = q_pos0 + n_q);
+ *     0 = every key visible, window on |n - m|.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * Requires n_q >= 0, n_kv >= 1, q_pos0 >= 0, h_q % h_kv == 0 without a map,
+ * rope_base > 1, k_turns > 0 when window_on.  n_q = 0 launches nothing.
+ */
+int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0,
+                int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                const int64_t* o_strides,
+                double rope_base, double k_turns, int32_t causal, int32_t window_on,
+                double softmax_scale, void* stream);
+
+/*
+ * atw_decode -- one query token per sequence against a pre-RoPE KV cache,
+ * split over the key axis (split-KV) and merged by a combine pass.  The
+ * window acts in the key loads: for each key only the pair slice inside the
+ * window at that key's distance is read ("The idea": the out-of-window prefix
+ * of a key is never loaded).
+ *
+ *   q       [batch, h_q, head_dim]           strides q_strides[2] (batch, head)
+ *   k_cache [batch, h_kv, L, head_dim]       strides k_strides[3] (batch, head, token)
+ *   v_cache [batch, h_kv, L, head_dim]       strides v_strides[3]
+ *   o       [batch, h_q, head_dim]           strides o_strides[2], written
+ *   kv_len  host int64 [batch]: keys 0..kv_len[b]-1 of sequence b are valid (>= 1)
+ *   q_pos   host int64 [batch]: position of sequence b's query; causal
+ *           requires q_pos[b] >= kv_len[b] - 1 (all cached keys visible).
+ *   num_splits: key-axis splits per (sequence, kv head), 1..1024; each split
+ *           covers ceil(kv_len/num_splits) keys.
+ *   workspace: device buffer of at least atw_decode_workspace_bytes(...)
+ *           bytes for the per-split partial results (max, sum, unnormalised
+ *           output); contents on entry are ignored.
+ * batch <= 256.  dtype must be ATW_BF16.
+ */
+int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+               int64_t batch, const int64_t* kv_len, const int64_t* q_pos,
+               int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+               const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+               const int64_t* o_strides,
+               double rope_base, double k_turns, int32_t causal, int32_t window_on,
+               double softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Workspace bytes atw_decode needs: batch * h_q * num_splits * (head_dim + 2) * 4. */
+size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits);
+
+/*
+ * atw_pruned_terms -- host only.  Number of pruned and total pair-terms
+ * (one term = one (query, key, pair) triple) per (batch, query head) over the
+ * visible cells of a prefill call with the same arguments (decode: n_q = 1,
+ * q_pos0 = q_pos, n_kv = kv_len).  Exact closed form (one arithmetic series
+ * per pair), input independent ("The idea": the cost is known before
+ * running).  Writes *pruned and *total.
+ */
+int atw_pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim,
+                     double rope_base, double k_turns, int32_t causal, int32_t window_on,
+                     int64_t* pruned, int64_t* total);
+
+/*
+ * atw_window_widths -- host only.  Integer windows W_r = floor(k * 2*pi /
+ * theta_r), r = 0..head_dim/2-1, computed in IEEE double and written to
+ * widths_out (host int64 [head_dim/2]); ATW_UNBOUNDED when the window is off
+ * or k = +inf.  Any even head_dim in 2..256 is accepted.
+ */
+int atw_window_widths(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                      int64_t* widths_out);
+
+/*
+ * atw_window_plan -- host only.  Tile plan ("Porting to something else": the
+ * retained prefix per key tile): for query tile a (rows a*tile_q ...) and key
+ * tile b (keys b*tile_k ...) writes plan_out[(a*n_kt + b)*2 + {0,1}] =
+ * (r_any, r_full): pairs below r_any are pruned for every visible cell of the
+ * tile, pairs from r_full on are kept for every visible cell; (-1, -1) for a
+ * tile without a visible cell.  n_qt = ceil(n_q/tile_q), n_kt =
+ * ceil(n_kv/tile_k); plan_out is host int32 [n_qt * n_kt * 2].
+ */
+int atw_window_plan(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                    int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t causal,
+                    int32_t tile_q, int32_t tile_k, int32_t* plan_out);
+
+/*
+ * atw_window_plan_device -- the same tile plan, computed on the GPU by the
+ * device code the prefill kernels use for their per-tile pair ranges and
+ * per-cell pair masks.  plan_out: device int32 [n_qt * n_kt * 2] as above;
+ * pruned_out: device int64 [n_qt * n_kt], the number of pruned pair-terms of
+ * each tile as the kernels' masks count them (sums to atw_pruned_terms).
+ * n_q * n_kv must be <= 2^40.  Asynchronous on stream.
+ */
+int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                           int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t causal,
+                           int32_t tile_q, int32_t tile_k, int32_t* plan_out, int64_t* pruned_out,
+                           void* stream);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* atw_last_error(void);
+
+/* Library version string. */
+const char* atw_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATW_H */

@@ -1,0 +1,30 @@
+"""rope_frequency_pair_amd -- per-RoPE-wavelength attention windows on MI355X.
+
+Causal softmax attention in which RoPE frequency pair r contributes to a
+query-key score only while the query-key distance is within k wavelengths of
+that pair ("ATFlash — Per-RoPE-Wavelength Attention Windows", README, "The
+idea").  The work runs in hand-written HIP kernels for gfx950 behind the C
+ABI of ``libatw.so`` (``include/atw.h``); this package is the thin Python
+binding (argument marshalling only) plus the build script.
+
+    from rope_frequency_pair_amd import prefill, decode, pruned_terms
+"""
+
+from .binding import (  # noqa: F401
+    ATW_BF16,
+    ATW_F32,
+    EXPORTED,
+    LIB_PATH,
+    UNBOUNDED,
+    AtwError,
+    decode,
+    decode_workspace_bytes,
+    default_scale,
+    load_library,
+    prefill,
+    pruned_terms,
+    version,
+    window_plan,
+    window_plan_device,
+    window_widths,
+)

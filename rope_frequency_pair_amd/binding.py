@@ -1,0 +1,213 @@
+"""ctypes binding of libatw (include/atw.h): argument marshalling only.
+
+Every computation runs in the HIP library; PyTorch supplies device memory
+and the current stream.  If libatw.so is missing the functions raise -- there
+is no fallback implementation.
+"""
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libatw.so")
+
+ATW_OK, ATW_EINVAL, ATW_EUNSUPPORTED, ATW_EWORKSPACE, ATW_EHIP = 0, -1, -2, -3, -4
+ATW_F32, ATW_BF16 = 0, 1
+UNBOUNDED = 1 << 62
+
+EXPORTED = [
+    "atw_prefill", "atw_decode", "atw_decode_workspace_bytes", "atw_pruned_terms",
+    "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
+    "atw_version",
+]
+
+
+class AtwError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"atw error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+_i32, _i64, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+def load_library(path=LIB_PATH):
+    """Load libatw.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run rope_frequency_pair_amd.build.build() "
+                           "(hipcc, gfx950) first; there is no fallback path")
+    lib = ctypes.CDLL(path)
+    lib.atw_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _pi32,
+                                _i32, _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _vp]
+    lib.atw_prefill.restype = ctypes.c_int
+    lib.atw_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _pi64, _pi64, _i32, _i32, _pi32, _i32,
+                               _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _i32, _vp,
+                               ctypes.c_size_t, _vp]
+    lib.atw_decode.restype = ctypes.c_int
+    lib.atw_decode_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
+    lib.atw_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.atw_pruned_terms.argtypes = [_i64, _i64, _i64, _i32, _f64, _f64, _i32, _i32, _pi64, _pi64]
+    lib.atw_pruned_terms.restype = ctypes.c_int
+    lib.atw_window_widths.argtypes = [_i32, _f64, _f64, _i32, _pi64]
+    lib.atw_window_widths.restype = ctypes.c_int
+    lib.atw_window_plan.argtypes = [_i32, _f64, _f64, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _pi32]
+    lib.atw_window_plan.restype = ctypes.c_int
+    lib.atw_window_plan_device.argtypes = [_i32, _f64, _f64, _i32, _i64, _i64, _i64, _i32, _i32, _i32,
+                                           _vp, _vp, _vp]
+    lib.atw_window_plan_device.restype = ctypes.c_int
+    lib.atw_last_error.argtypes = []
+    lib.atw_last_error.restype = ctypes.c_char_p
+    lib.atw_version.argtypes = []
+    lib.atw_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(code):
+    if code != ATW_OK:
+        raise AtwError(code, _lib.atw_last_error().decode())
+
+
+def _arr64(vals):
+    vals = list(vals)
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _arr32(vals):
+    vals = list(vals)
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATW_BF16
+    if t.dtype == torch.float32:
+        return ATW_F32
+    raise AtwError(ATW_EUNSUPPORTED, f"unsupported dtype {t.dtype}")
+
+
+def _head_map(kv_head_of_q):
+    if kv_head_of_q is None:
+        return None
+    return _arr32(int(x) for x in kv_head_of_q)
+
+
+def version():
+    return load_library().atw_version().decode()
+
+
+def window_widths(head_dim, rope_base, k_turns, window_on=True):
+    """Integer windows W_r (list of int) computed by the library."""
+    lib = load_library()
+    out = (ctypes.c_int64 * (head_dim // 2))()
+    _check(lib.atw_window_widths(head_dim, float(rope_base), float(k_turns), int(window_on), out))
+    return list(out)
+
+
+def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, window_on=True):
+    """(pruned, total) pair-term counts per (batch, query head)."""
+    lib = load_library()
+    p, t = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.atw_pruned_terms(n_q, n_kv, q_pos0, head_dim, float(rope_base), float(k_turns),
+                                int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
+    return p.value, t.value
+
+
+def window_plan(head_dim, rope_base, k_turns, window_on, n_q, n_kv, q_pos0, causal, tile_q, tile_k):
+    """Host tile plan as a nested list [n_qt][n_kt] of (r_any, r_full)."""
+    lib = load_library()
+    n_qt, n_kt = -(-n_q // tile_q), -(-n_kv // tile_k)
+    buf = (ctypes.c_int32 * (2 * n_qt * n_kt))()
+    _check(lib.atw_window_plan(head_dim, float(rope_base), float(k_turns), int(window_on), n_q, n_kv,
+                               q_pos0, int(causal), tile_q, tile_k, buf))
+    return [[(buf[(a * n_kt + b) * 2], buf[(a * n_kt + b) * 2 + 1]) for b in range(n_kt)]
+            for a in range(n_qt)]
+
+
+def window_plan_device(head_dim, rope_base, k_turns, window_on, n_q, n_kv, q_pos0, causal, tile_q,
+                       tile_k, stream=None):
+    """Tile plan and per-tile pruned counts computed by the GPU's device code.
+
+    Returns (plan int32 [n_qt, n_kt, 2], pruned int64 [n_qt, n_kt]) as CUDA tensors.
+    """
+    import torch
+    lib = load_library()
+    n_qt, n_kt = -(-n_q // tile_q), -(-n_kv // tile_k)
+    plan = torch.empty((n_qt, n_kt, 2), dtype=torch.int32, device="cuda")
+    pruned = torch.empty((n_qt, n_kt), dtype=torch.int64, device="cuda")
+    _check(lib.atw_window_plan_device(head_dim, float(rope_base), float(k_turns), int(window_on), n_q,
+                                      n_kv, q_pos0, int(causal), tile_q, tile_k,
+                                      ctypes.c_void_p(plan.data_ptr()),
+                                      ctypes.c_void_p(pruned.data_ptr()), _stream_ptr(stream)))
+    return plan, pruned
+
+
+def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=True, scale=None,
+            kv_head_of_q=None, out=None, stream=None):
+    """Windowed prefill.  q [B, Hq, Nq, d]; k, v [B, Hkv, Nkv, d] (any strides
+    with d contiguous), bf16 or fp32 CUDA tensors.  Returns out [B, Hq, Nq, d]."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise AtwError(ATW_EINVAL, f"{name} must be 4-D with a contiguous last dim")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    _check(lib.atw_prefill(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
+        _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
+        _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), float(rope_base), float(k_turns),
+        int(causal), int(window_on), float(scale or 0.0), _stream_ptr(stream)))
+    return out
+
+
+def decode_workspace_bytes(batch, h_q, head_dim, num_splits):
+    return load_library().atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits)
+
+
+def decode(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=True, window_on=True,
+           scale=None, num_splits=64, kv_head_of_q=None, workspace=None, out=None, stream=None):
+    """Windowed split-KV decode.  q [B, Hq, d]; caches [B, Hkv, L, d] bf16 CUDA
+    tensors; kv_len, q_pos: per-sequence ints.  Returns out [B, Hq, d]."""
+    import torch
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    need = lib.atw_decode_workspace_bytes(B, Hq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
+    q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
+    _check(lib.atw_decode(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
+        _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
+        _arr64(out.stride()[:2]), float(rope_base), float(k_turns), int(causal), int(window_on),
+        float(scale or 0.0), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return out
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,310 @@
+// C ABI of libatw (declared in include/atw.h): argument checks, the window
+// planner, and the kernel launches.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/atw.h"
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATW_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_window(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                 int max_dim) {
+  if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > max_dim)
+    return fail(ATW_EINVAL, "head_dim must be even and in 2..%d (got %d)", max_dim, head_dim);
+  if (!(rope_base > 1.0) || std::isinf(rope_base))
+    return fail(ATW_EINVAL, "rope_base must be a finite value > 1 (got %g)", rope_base);
+  if (window_on && !(k_turns > 0.0))
+    return fail(ATW_EINVAL, "k_turns must be > 0 when the window is on (got %g)", k_turns);
+  return ATW_OK;
+}
+
+// Kernel view of the window: W_r clamped to INT32_MAX and turns per position.
+void fill_window(atw::WindowArgs* w, int head_dim, double rope_base, double k_turns, bool on) {
+  int64_t widths[atw::kMaxHeadDim / 2];
+  atw::window_widths(head_dim, rope_base, k_turns, on, widths);
+  double phi[atw::kMaxHeadDim / 2];
+  atw::pair_turns_per_position(head_dim, rope_base, phi);
+  for (int r = 0; r < atw::kMaxPairs; ++r) {
+    if (r < head_dim / 2) {
+      w->w[r] = widths[r] > (int64_t)atw::kWindowInf ? atw::kWindowInf : (int32_t)widths[r];
+      w->phi[r] = phi[r];
+    } else {
+      w->w[r] = atw::kWindowInf;
+      w->phi[r] = 0.0;
+    }
+  }
+}
+
+int check_heads(int32_t h_q, int32_t h_kv, const int32_t* map, int16_t* out) {
+  if (h_q <= 0 || h_kv <= 0) return fail(ATW_EINVAL, "h_q and h_kv must be positive");
+  if (h_q > atw::kMaxHeadsQ || h_kv > atw::kMaxHeadsQ)
+    return fail(ATW_EUNSUPPORTED, "h_q and h_kv must be <= %d", atw::kMaxHeadsQ);
+  if (map == nullptr) {
+    if (h_q % h_kv != 0)
+      return fail(ATW_EINVAL, "h_q (%d) must be a multiple of h_kv (%d) without a head map", h_q, h_kv);
+    for (int h = 0; h < h_q; ++h) out[h] = (int16_t)(h / (h_q / h_kv));
+  } else {
+    for (int h = 0; h < h_q; ++h) {
+      if (map[h] < 0 || map[h] >= h_kv)
+        return fail(ATW_EINVAL, "kv_head_of_q[%d] = %d is outside [0, %d)", h, map[h], h_kv);
+      out[h] = (int16_t)map[h];
+    }
+  }
+  return ATW_OK;
+}
+
+int check_strides(const char* name, const int64_t* s, int n, int elem) {
+  if (s == nullptr) return fail(ATW_EINVAL, "%s_strides is NULL", name);
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(ATW_EINVAL, "%s_strides[%d] is negative", name, i);
+    if ((s[i] * elem) % 16 != 0)
+      return fail(ATW_EUNSUPPORTED, "%s_strides[%d] = %lld is not a multiple of 16 bytes", name, i,
+                  (long long)s[i]);
+  }
+  return ATW_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATW_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* atw_last_error(void) { return g_last_error.c_str(); }
+
+const char* atw_version(void) { return "atw 0.1 (gfx950)"; }
+
+int atw_window_widths(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                      int64_t* widths_out) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  if (widths_out == nullptr) return fail(ATW_EINVAL, "widths_out is NULL");
+  atw::window_widths(head_dim, rope_base, k_turns, window_on != 0, widths_out);
+  return ok();
+}
+
+int atw_pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim, double rope_base,
+                     double k_turns, int32_t causal, int32_t window_on, int64_t* pruned,
+                     int64_t* total) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  if (pruned == nullptr || total == nullptr) return fail(ATW_EINVAL, "pruned/total is NULL");
+  if (n_q < 0 || n_kv < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "n_q, n_kv, q_pos0 must be >= 0");
+  if (n_q > (int64_t(1) << 40) || n_kv > (int64_t(1) << 40) || q_pos0 > (int64_t(1) << 40))
+    return fail(ATW_EINVAL, "sizes above 2^40 are not supported");
+  int64_t w[atw::kMaxHeadDim / 2];
+  atw::window_widths(head_dim, rope_base, k_turns, window_on != 0, w);
+  atw::pruned_terms(n_q, n_kv, q_pos0, head_dim, w, causal != 0, pruned, total);
+  return ok();
+}
+
+int atw_window_plan(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                    int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t causal, int32_t tile_q,
+                    int32_t tile_k, int32_t* plan_out) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  if (plan_out == nullptr) return fail(ATW_EINVAL, "plan_out is NULL");
+  if (n_q < 0 || n_kv < 0 || q_pos0 < 0 || tile_q <= 0 || tile_k <= 0)
+    return fail(ATW_EINVAL, "sizes must be >= 0 and tiles > 0");
+  int64_t w[atw::kMaxHeadDim / 2];
+  atw::window_widths(head_dim, rope_base, k_turns, window_on != 0, w);
+  atw::tile_plan(head_dim, w, n_q, n_kv, q_pos0, causal != 0, tile_q, tile_k, plan_out);
+  return ok();
+}
+
+int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
+                           int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t causal,
+                           int32_t tile_q, int32_t tile_k, int32_t* plan_out, int64_t* pruned_out,
+                           void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, 2 * atw::kMaxPairs)) return e;
+  if (plan_out == nullptr || pruned_out == nullptr) return fail(ATW_EINVAL, "output is NULL");
+  if (n_q < 0 || n_kv < 0 || q_pos0 < 0 || tile_q <= 0 || tile_k <= 0)
+    return fail(ATW_EINVAL, "sizes must be >= 0 and tiles > 0");
+  if (n_q * n_kv > (int64_t(1) << 40) || q_pos0 + n_q >= (int64_t(1) << 31) ||
+      n_kv >= (int64_t(1) << 31))
+    return fail(ATW_EINVAL, "n_q * n_kv must be <= 2^40 and positions < 2^31");
+  atw::PlanParams p{};
+  p.plan = plan_out;
+  p.pruned = pruned_out;
+  p.n_q = n_q;
+  p.n_kv = n_kv;
+  p.q_pos0 = q_pos0;
+  p.causal = causal != 0;
+  p.tile_q = tile_q;
+  p.tile_k = tile_k;
+  p.h = head_dim / 2;
+  p.n_qt = (n_q + tile_q - 1) / tile_q;
+  p.n_kt = (n_kv + tile_k - 1) / tile_k;
+  fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
+  return hip_status(atw::launch_plan(p, (hipStream_t)stream), "plan kernel launch");
+}
+
+int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t batch,
+                int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q, int32_t h_kv,
+                const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
+                const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                double rope_base, double k_turns, int32_t causal, int32_t window_on,
+                double softmax_scale, void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ATW_EUNSUPPORTED, "prefill supports head_dim 64 and 128 (got %d)", head_dim);
+  if (dtype != ATW_F32 && dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "dtype must be ATW_F32 or ATW_BF16");
+  if (batch <= 0 || n_q < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "batch > 0, n_q >= 0, q_pos0 >= 0 required");
+  if (n_kv < 1) return fail(ATW_EINVAL, "n_kv must be >= 1");
+  if (q_pos0 + n_q >= (int64_t(1) << 31) || n_kv >= (int64_t(1) << 31))
+    return fail(ATW_EUNSUPPORTED, "positions must be < 2^31");
+  if (!std::isfinite(softmax_scale)) return fail(ATW_EINVAL, "softmax_scale must be finite");
+  int16_t kvh[atw::kMaxHeadsQ];
+  if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
+  if (n_q == 0) return ok();   // nothing to compute; empty tensors may have NULL data
+  if (!q || !k || !v || !o) return fail(ATW_EINVAL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATW_EUNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+  const int elem = dtype == ATW_BF16 ? 2 : 4;
+  if (int e = check_strides("q", q_strides, 3, elem)) return e;
+  if (int e = check_strides("k", k_strides, 3, elem)) return e;
+  if (int e = check_strides("v", v_strides, 3, elem)) return e;
+  if (int e = check_strides("o", o_strides, 3, elem)) return e;
+  const int64_t n_qblk = (n_q + atw::kPrefillBlockRows - 1) / atw::kPrefillBlockRows;
+  if (n_qblk * h_q * batch >= (int64_t(1) << 31)) return fail(ATW_EUNSUPPORTED, "grid too large");
+
+  atw::PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = q_strides[i];
+    p.ks[i] = k_strides[i];
+    p.vs[i] = v_strides[i];
+    p.os[i] = o_strides[i];
+  }
+  p.batch = (int32_t)batch;
+  p.n_q = (int32_t)n_q;
+  p.n_kv = (int32_t)n_kv;
+  p.q_pos0 = (int32_t)q_pos0;
+  p.h_q = h_q;
+  p.causal = causal != 0;
+  p.n_qblk = (int32_t)n_qblk;
+  const double scale = softmax_scale > 0 ? softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  for (int h = 0; h < h_q; ++h) p.kvh[h] = kvh[h];
+  fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
+  return hip_status(atw::launch_prefill(p, dtype, head_dim, (hipStream_t)stream), "prefill launch");
+}
+
+size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits) {
+  if (batch <= 0 || h_q <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return (size_t)batch * (size_t)h_q * (size_t)num_splits * (size_t)(head_dim + 4) * sizeof(float);
+}
+
+int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+               int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+               int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+               const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+               const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
+               int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ATW_EUNSUPPORTED, "decode supports head_dim 64 and 128 (got %d)", head_dim);
+  if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 only");
+  if (batch <= 0 || batch > atw::kMaxDecodeBatch)
+    return fail(ATW_EUNSUPPORTED, "batch must be in 1..%d", atw::kMaxDecodeBatch);
+  if (num_splits <= 0 || num_splits > 1024) return fail(ATW_EINVAL, "num_splits must be in 1..1024");
+  if (!std::isfinite(softmax_scale)) return fail(ATW_EINVAL, "softmax_scale must be finite");
+  if (kv_len == nullptr || q_pos == nullptr) return fail(ATW_EINVAL, "kv_len and q_pos must be non-NULL");
+  for (int64_t b = 0; b < batch; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] >= (int64_t(1) << 31))
+      return fail(ATW_EINVAL, "kv_len[%lld] = %lld must be in 1..2^31-1", (long long)b, (long long)kv_len[b]);
+    if (q_pos[b] < 0 || q_pos[b] >= (int64_t(1) << 31))
+      return fail(ATW_EINVAL, "q_pos[%lld] out of range", (long long)b);
+    if (causal && q_pos[b] < kv_len[b] - 1)
+      return fail(ATW_EINVAL, "causal decode needs q_pos[%lld] >= kv_len - 1", (long long)b);
+  }
+  int16_t kvh[atw::kMaxHeadsQ];
+  if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
+  if (!q || !k_cache || !v_cache || !o) return fail(ATW_EINVAL, "q, k_cache, v_cache and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATW_EUNSUPPORTED, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (int e = check_strides("q", q_strides, 2, 2)) return e;
+  if (int e = check_strides("k", k_strides, 3, 2)) return e;
+  if (int e = check_strides("v", v_strides, 3, 2)) return e;
+  if (o_strides == nullptr || o_strides[0] < 0 || o_strides[1] < 0)
+    return fail(ATW_EINVAL, "o_strides must be non-NULL and non-negative");
+  const size_t need = atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATW_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(ATW_EUNSUPPORTED, "workspace must be 16-byte aligned");
+
+  atw::DecodeParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.ws = static_cast<float*>(workspace);
+  p.qs[0] = q_strides[0];
+  p.qs[1] = q_strides[1];
+  p.os[0] = o_strides[0];
+  p.os[1] = o_strides[1];
+  for (int i = 0; i < 3; ++i) {
+    p.ks[i] = k_strides[i];
+    p.vs[i] = v_strides[i];
+  }
+  p.batch = (int32_t)batch;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.splits = num_splits;
+  p.causal = causal != 0;
+  const double scale = softmax_scale > 0 ? softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  for (int64_t b = 0; b < batch; ++b) {
+    p.kv_len[b] = (int32_t)kv_len[b];
+    p.q_pos[b] = (int32_t)q_pos[b];
+  }
+  // group query heads by kv head; a kv head may serve at most 32 query heads
+  int n = 0;
+  for (int kv = 0; kv < h_kv; ++kv) {
+    p.kv_first[kv] = (int16_t)n;
+    int cnt = 0;
+    for (int h = 0; h < h_q; ++h)
+      if (kvh[h] == kv) {
+        p.qh_of_kv[n++] = (int16_t)h;
+        ++cnt;
+      }
+    if (cnt > 32) return fail(ATW_EUNSUPPORTED, "decode supports at most 32 query heads per kv head");
+  }
+  p.kv_first[h_kv] = (int16_t)n;
+  p.group = h_q / h_kv;
+  fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
+  return hip_status(atw::launch_decode(p, head_dim, (hipStream_t)stream), "decode launch");
+}
+
+}  // extern "C"

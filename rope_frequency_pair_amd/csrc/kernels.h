@@ -1,0 +1,65 @@
+// Kernel parameter blocks and launchers (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace atw {
+
+constexpr int kMaxHeadsQ = 256;
+constexpr int kMaxDecodeBatch = 256;
+
+// Prefill: one workgroup = 256 consecutive query rows of one query head;
+// 8 waves of 32 rows; key tiles of 64.
+constexpr int kPrefillBlockRows = 256;
+constexpr int kPrefillTileK = 64;
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];   // element strides (batch, head, token)
+  int32_t batch, n_q, n_kv, q_pos0;
+  int32_t h_q, causal, n_qblk, pad0;
+  float scale_log2;                      // softmax scale * log2(e)
+  int16_t kvh[kMaxHeadsQ];               // kv head of each query head
+  WindowArgs win;
+};
+
+// Decode: split-KV over the key axis, then a combine pass.
+constexpr int kDecodeTileK = 64;
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* ws;                             // [batch, h_q, splits, head_dim + 2]
+  int64_t qs[2], ks[3], vs[3], os[2];
+  int32_t batch, h_q, h_kv, splits;
+  int32_t causal, group, pad0, pad1;     // group = query heads per kv head
+  float scale_log2;
+  int32_t kv_len[kMaxDecodeBatch];
+  int32_t q_pos[kMaxDecodeBatch];
+  int16_t qh_of_kv[kMaxHeadsQ];          // query heads grouped by kv head (kv-major)
+  int16_t kv_first[kMaxHeadsQ + 1];      // start of each kv head's group in qh_of_kv
+  WindowArgs win;
+};
+
+struct PlanParams {
+  int32_t* plan;
+  int64_t* pruned;
+  int64_t n_q, n_kv, q_pos0;
+  int32_t causal, tile_q, tile_k, h;
+  int64_t n_qt, n_kt;
+  WindowArgs win;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+
+}  // namespace atw

@@ -1,0 +1,130 @@
+// Host-side window planner (see planner.h).
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace atw {
+
+void window_widths(int head_dim, double rope_base, double k_turns, bool window_on, int64_t* w) {
+  const int h = head_dim / 2;
+  if (!window_on || std::isinf(k_turns)) {
+    for (int r = 0; r < h; ++r) w[r] = kUnbounded;
+    return;
+  }
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (int r = 0; r < h; ++r) {
+    // same operation order as the definition: theta, wavelength, k * wavelength
+    const double theta = std::pow(rope_base, (-2.0 * r) / head_dim);
+    const double lam = two_pi / theta;
+    const double x = std::floor(k_turns * lam);
+    w[r] = (x >= 4611686018427387904.0) ? kUnbounded : static_cast<int64_t>(x);
+  }
+}
+
+void pair_turns_per_position(int head_dim, double rope_base, double* phi) {
+  const int h = head_dim / 2;
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (int r = 0; r < h; ++r) phi[r] = std::pow(rope_base, (-2.0 * r) / head_dim) / two_pi;
+}
+
+int first_retained_pair(const int64_t* w, int h, int64_t delta) {
+  // w is sorted; count of entries < delta
+  return static_cast<int>(std::lower_bound(w, w + h, delta) - w);
+}
+
+namespace {
+
+using i128 = __int128;
+
+// sum_{x=a}^{b-1} x  (0 if b <= a)
+i128 series(i128 a, i128 b) {
+  if (b <= a) return 0;
+  return (a + b - 1) * (b - a) / 2;
+}
+
+// sum over rows n in [A, B) of clamp(n - W, 0, n_kv): the number of causal
+// cells of row n at distance > W (row n sees distances max(0,n-n_kv+1)..n).
+i128 causal_pruned_rows(i128 A, i128 B, i128 W, i128 n_kv) {
+  // n <= W: 0;  W < n < W + n_kv: n - W;  n >= W + n_kv: n_kv
+  const i128 lo = std::max(A, W + 1), hi = std::min(B, W + n_kv);
+  i128 s = series(lo - W, hi - W);
+  const i128 full_lo = std::max(A, W + n_kv);
+  if (B > full_lo) s += (B - full_lo) * n_kv;
+  return s;
+}
+
+// sum over rows n in [A, B) of #{m in [0, n_kv): m - n > W} = clamp(K - n, 0, .)
+// with K = n_kv - 1 - W (non-causal, keys after the query).
+i128 noncausal_after_rows(i128 A, i128 B, i128 W, i128 n_kv) {
+  const i128 K = n_kv - 1 - W;
+  const i128 hi = std::min(B, K);
+  if (hi <= A) return 0;
+  // sum_{n=A}^{hi-1} (K - n) = sum_{x=K-hi+1}^{K-A} x
+  return series(K - hi + 1, K - A + 1);
+}
+
+}  // namespace
+
+void pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
+                  bool causal, int64_t* pruned, int64_t* total) {
+  const int h = head_dim / 2;
+  if (n_q <= 0 || n_kv <= 0) {
+    *pruned = 0;
+    *total = 0;
+    return;
+  }
+  const i128 A = q_pos0, B = (i128)q_pos0 + n_q, NKV = n_kv;
+  i128 p = 0, visible;
+  if (causal) {
+    // row n sees min(n + 1, n_kv) keys
+    const i128 split = std::min(B, std::max(A, NKV - 1));  // rows n < n_kv - 1 see n + 1
+    visible = series(A + 1, split + 1) + (B - split) * NKV;
+    for (int r = 0; r < h; ++r) p += causal_pruned_rows(A, B, w[r], NKV);
+  } else {
+    visible = (i128)n_q * NKV;
+    for (int r = 0; r < h; ++r)
+      p += causal_pruned_rows(A, B, w[r], NKV) + noncausal_after_rows(A, B, w[r], NKV);
+  }
+  *pruned = static_cast<int64_t>(p);
+  *total = static_cast<int64_t>(visible * h);
+}
+
+bool tile_distance_range(int64_t n_lo, int64_t n_hi, int64_t m_lo, int64_t m_hi, bool causal,
+                         int64_t* dmin, int64_t* dmax) {
+  if (n_hi < n_lo || m_hi < m_lo) return false;
+  if (causal) {
+    if (m_lo > n_hi) return false;
+    *dmin = std::max<int64_t>(0, n_lo - m_hi);
+    *dmax = n_hi - m_lo;
+  } else {
+    if (m_hi < n_lo) *dmin = n_lo - m_hi;
+    else if (m_lo > n_hi) *dmin = m_lo - n_hi;
+    else *dmin = 0;
+    *dmax = std::max(std::abs(n_hi - m_lo), std::abs(n_lo - m_hi));
+  }
+  return true;
+}
+
+void tile_plan(int head_dim, const int64_t* w, int64_t n_q, int64_t n_kv, int64_t q_pos0,
+               bool causal, int tile_q, int tile_k, int32_t* plan) {
+  const int h = head_dim / 2;
+  const int64_t n_qt = (n_q + tile_q - 1) / tile_q, n_kt = (n_kv + tile_k - 1) / tile_k;
+  for (int64_t a = 0; a < n_qt; ++a) {
+    const int64_t n_lo = q_pos0 + a * tile_q;
+    const int64_t n_hi = q_pos0 + std::min<int64_t>((a + 1) * tile_q, n_q) - 1;
+    for (int64_t b = 0; b < n_kt; ++b) {
+      const int64_t m_lo = b * tile_k, m_hi = std::min<int64_t>((b + 1) * tile_k, n_kv) - 1;
+      int32_t* out = plan + (a * n_kt + b) * 2;
+      int64_t dmin, dmax;
+      if (!tile_distance_range(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
+        out[0] = out[1] = -1;
+        continue;
+      }
+      out[0] = first_retained_pair(w, h, dmin);
+      out[1] = first_retained_pair(w, h, dmax);
+    }
+  }
+}
+
+}  // namespace atw

@@ -1,0 +1,44 @@
+// Host-side window planner: integer windows, pruned-term counts, tile plans.
+//
+// Definitions: "ATFlash — Per-RoPE-Wavelength Attention Windows", README,
+// "The idea" (pair r turns by (n-m)*theta_r; its term is zero beyond the
+// distance w_r = k*lambda_r; the reduction is input independent and known in
+// closed form before running) and "Porting to something else" (per key tile,
+// the prefix of pairs that is never needed).
+#pragma once
+
+#include <cstdint>
+
+namespace atw {
+
+constexpr int kMaxHeadDim = 256;
+constexpr int64_t kUnbounded = int64_t(1) << 62;
+
+// W_r = floor(k * 2*pi / theta_r), theta_r = base^(-2r/d), in IEEE double;
+// kUnbounded when the window is off, k = +inf, or the value reaches 2^62.
+void window_widths(int head_dim, double rope_base, double k_turns, bool window_on, int64_t* w);
+
+// theta_r / (2*pi): turns per position of pair r.
+void pair_turns_per_position(int head_dim, double rope_base, double* phi);
+
+// Number of pairs whose window is shorter than delta (pairs pruned at that
+// distance).  w is non-decreasing; h entries.
+int first_retained_pair(const int64_t* w, int h, int64_t delta);
+
+// Exact (pruned, total) pair-term counts per (batch, query head): query i at
+// position q_pos0 + i, key j at position j, visible iff j <= position (causal)
+// or always (non-causal).  Closed form: one arithmetic series per pair.
+void pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
+                  bool causal, int64_t* pruned, int64_t* total);
+
+// Smallest and largest distance over the visible cells of the tile
+// rows [n_lo, n_hi] x keys [m_lo, m_hi] (positions).  Returns false when the
+// tile has no visible cell.
+bool tile_distance_range(int64_t n_lo, int64_t n_hi, int64_t m_lo, int64_t m_hi, bool causal,
+                         int64_t* dmin, int64_t* dmax);
+
+// Tile plan (r_any, r_full) per (query tile, key tile); (-1, -1) if empty.
+void tile_plan(int head_dim, const int64_t* w, int64_t n_q, int64_t n_kv, int64_t q_pos0,
+               bool causal, int tile_q, int tile_k, int32_t* plan);
+
+}  // namespace atw

@@ -1,0 +1,164 @@
+"""Host-side tests of libatw (no GPU needed): the library loads, exports every
+symbol include/atw.h declares, and its planner matches the oracle bit-exactly
+(integer windows, pruned/total counts, tile plans); invalid arguments return
+the documented codes before any launch."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import rope_frequency_pair_amd as atw
+from rope_frequency_pair_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(atw.LIB_PATH):
+        pytest.skip("libatw.so not built (run __graft_entry__.build())")
+    return atw.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "atw.h")).read()
+    declared = set(re.findall(r"\b(atw_[a-z_]+)\s*\(", header))
+    assert declared == set(binding.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in atw.version()
+
+
+WINDOW_CASES = [(64, 1e4, 4.0), (64, 1e6, 8.0), (128, 5e5, 8.0), (128, 1e7, 8.0), (128, 1e7, 64.0),
+                (2, 10.0, 0.5), (16, 50.0, 1.0), (256, 1e4, 3.0), (96, 123456.0, 0.37)]
+
+
+@pytest.mark.parametrize("d,base,k", WINDOW_CASES)
+def test_widths_bit_exact(lib, d, base, k):
+    assert atw.window_widths(d, base, k, True) == list(oracle.window_widths(d, base, k, True))
+    assert atw.window_widths(d, base, k, False) == [atw.UNBOUNDED] * (d // 2)
+    assert atw.window_widths(d, base, math.inf, True) == [atw.UNBOUNDED] * (d // 2)
+
+
+def test_widths_random_grid_bit_exact(lib):
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        d = int(rng.choice([2, 8, 32, 64, 128, 256]))
+        base = float(10 ** rng.uniform(0.5, 9))
+        k = float(10 ** rng.uniform(-2, 3))
+        assert atw.window_widths(d, base, k) == list(oracle.window_widths(d, base, k)), (d, base, k)
+
+
+def test_counts_bit_exact_small(lib):
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        d = int(rng.choice([2, 4, 8, 16, 64]))
+        base = float(rng.choice([3.0, 10.0, 100.0, 1e4]))
+        k = float(rng.choice([0.01, 0.2, 0.5, 1.0, 3.0]))
+        n_q, n_kv, p0 = int(rng.integers(0, 50)), int(rng.integers(0, 90)), int(rng.integers(0, 70))
+        causal, on = bool(rng.integers(0, 2)), bool(rng.integers(0, 4))
+        got = atw.pruned_terms(n_q, n_kv, p0, d, base, k, causal, on)
+        assert got == oracle.pruned_terms_bruteforce(n_q, n_kv, p0, d, base, k, causal, on)
+
+
+@pytest.mark.parametrize("n_q,n_kv,p0,d,base,k", [
+    (1024, 1024, 0, 64, 1e4, 4.0),
+    (32768, 32768, 0, 64, 1e6, 8.0),
+    (131072, 131072, 0, 128, 5e5, 8.0),
+    (1, 524288, 524288, 128, 1e7, 8.0),          # the decode row: query at L, keys 0..L-1
+    (65536, 1048576, 983040, 128, 1e7, 64.0),    # last 64K chunk of the 1M request
+    (1048576, 1048576, 0, 128, 1e7, 64.0),
+])
+def test_counts_bit_exact_workloads(lib, n_q, n_kv, p0, d, base, k):
+    for causal in (True, False):
+        got = atw.pruned_terms(n_q, n_kv, p0, d, base, k, causal, True)
+        assert got == oracle.pruned_terms(n_q, n_kv, p0, d, base, k, causal, True)
+
+
+def test_workload_count_values(lib):
+    # exact per-head counts of the five workloads (the square ones also equal
+    # the per-pair series of the oracle)
+    assert atw.pruned_terms(1024, 1024, 0, 64, 1e4, 4.0) == \
+        oracle.pruned_terms_square_closed_form(1024, 64, 1e4, 4.0)
+    p, t = atw.pruned_terms(131072, 131072, 0, 128, 5e5, 8.0)
+    assert (p, t) == oracle.pruned_terms_square_closed_form(131072, 128, 5e5, 8.0)
+    assert abs(p / t - 0.4930) < 1e-4
+    # 1M request = sum of its 16 chunks
+    tot_p = tot_t = 0
+    for c in range(16):
+        pp, tt = atw.pruned_terms(65536, 65536 * (c + 1), 65536 * c, 128, 1e7, 64.0)
+        tot_p += pp
+        tot_t += tt
+    assert (tot_p, tot_t) == oracle.pruned_terms_square_closed_form(1048576, 128, 1e7, 64.0)
+
+
+@pytest.mark.parametrize("n_q,n_kv,p0,causal,tq,tk", [
+    (300, 300, 0, True, 32, 64), (256, 1000, 744, True, 32, 64), (77, 200, 0, False, 16, 64),
+    (1024, 1024, 0, True, 256, 64), (33, 33, 5, True, 7, 9),
+])
+def test_tile_plan_bit_exact(lib, n_q, n_kv, p0, causal, tq, tk):
+    for d, base, k in [(64, 1e4, 4.0), (16, 100.0, 0.7), (128, 5e5, 0.1)]:
+        w = oracle.window_widths(d, base, k)
+        ref = oracle.tile_plan(n_q, n_kv, p0, causal, tq, tk, w)
+        got = np.array(atw.window_plan(d, base, k, True, n_q, n_kv, p0, causal, tq, tk), dtype=np.int32)
+        np.testing.assert_array_equal(got.reshape(ref.shape), ref)
+
+
+def test_invalid_arguments(lib):
+    c64 = ctypes.c_int64
+    p, t = c64(), c64()
+    # head_dim odd, base <= 1, k <= 0 with window on
+    assert lib.atw_pruned_terms(10, 10, 0, 63, 1e4, 4.0, 1, 1, ctypes.byref(p), ctypes.byref(t)) == atw.binding.ATW_EINVAL
+    assert lib.atw_pruned_terms(10, 10, 0, 64, 1.0, 4.0, 1, 1, ctypes.byref(p), ctypes.byref(t)) == atw.binding.ATW_EINVAL
+    assert lib.atw_pruned_terms(10, 10, 0, 64, 1e4, 0.0, 1, 1, ctypes.byref(p), ctypes.byref(t)) == atw.binding.ATW_EINVAL
+    assert b"k_turns" in lib.atw_last_error()
+    # k ignored when the window is off
+    assert lib.atw_pruned_terms(10, 10, 0, 64, 1e4, 0.0, 1, 0, ctypes.byref(p), ctypes.byref(t)) == 0
+    assert p.value == 0 and t.value == 32 * 55
+    # prefill argument errors are reported before touching any pointer
+    s = binding._arr64([0, 0, 0])
+    fake = ctypes.c_void_p(16)
+    args = dict(dtype=1, batch=1, n_q=10, n_kv=10, q_pos0=0, h_q=4, h_kv=2, d=128)
+
+    def pre(**kw):
+        a = dict(args, **kw)
+        return lib.atw_prefill(fake, fake, fake, fake, a["dtype"], a["batch"], a["n_q"], a["n_kv"],
+                               a["q_pos0"], a["h_q"], a["h_kv"], None, a["d"], s, s, s, s, 1e4, 4.0, 1,
+                               1, 0.0, None)
+
+    assert pre(d=96) == atw.binding.ATW_EUNSUPPORTED
+    assert pre(dtype=7) == atw.binding.ATW_EUNSUPPORTED
+    assert pre(h_q=3) == atw.binding.ATW_EINVAL
+    assert pre(n_kv=0) == atw.binding.ATW_EINVAL
+    assert pre(batch=0) == atw.binding.ATW_EINVAL
+    assert lib.atw_prefill(None, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, None, 128, s, s, s, s, 1e4,
+                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EINVAL
+    bad = binding._arr64([0, 0, 3])   # 3 bf16 elements = 6 bytes: not 16-byte multiple
+    assert lib.atw_prefill(fake, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, None, 128, bad, s, s, s, 1e4,
+                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EUNSUPPORTED
+    hmap = binding._arr32([0, 1, 2, 0])  # kv head 2 does not exist
+    assert lib.atw_prefill(fake, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, hmap, 128, s, s, s, s, 1e4,
+                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EINVAL
+
+
+def test_decode_invalid_arguments(lib):
+    s3, s2 = binding._arr64([0, 0, 0]), binding._arr64([0, 0])
+    fake = ctypes.c_void_p(16)
+    kv, qp = binding._arr64([100]), binding._arr64([99])
+    need = lib.atw_decode_workspace_bytes(1, 4, 128, 8)
+    assert need == 4 * 8 * (128 + 4) * 4
+
+    def dec(kv=kv, qp=qp, ws=need, causal=1, splits=8, dtype=1):
+        return lib.atw_decode(fake, fake, fake, fake, dtype, 1, kv, qp, 4, 2, None, 128, s2, s3, s3, s2,
+                              1e4, 4.0, causal, 1, 0.0, splits, fake, ws, None)
+
+    assert dec(ws=need - 1) == atw.binding.ATW_EWORKSPACE
+    assert dec(qp=binding._arr64([50])) == atw.binding.ATW_EINVAL      # causal needs q_pos >= kv_len-1
+    assert dec(kv=binding._arr64([0])) == atw.binding.ATW_EINVAL
+    assert dec(splits=0) == atw.binding.ATW_EINVAL
+    assert dec(dtype=0) == atw.binding.ATW_EUNSUPPORTED
