@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--quick", action="store_true", help="headline prefill only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -148,6 +150,13 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     w = synth.WORKLOADS[HEADLINE]
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
     log(f"[bench] {atw.version()} on {torch.cuda.get_device_name(0)}; inputs for {w.name}")
     q, k, v = synth.workload_prefill_inputs(w)
     out = torch.empty_like(q)
