@@ -40,7 +40,7 @@
  *     k = +inf with window_on = 1 gives the same result.
  *   - Supported on the GPU: head_dim 64 or 128; dtype ATW_BF16 (bf16 in and
  *     out, fp32 accumulation, bf16 MFMA) for prefill and decode, ATW_F32
- *     (fp32 in and out, fp32 MFMA) for prefill.  Positions must be < 2^31.
+ *     (fp32 in and out, fp32 MFMA) for prefill.  Positions must be < 2^30.
  */
 #ifndef ATW_H
 #define ATW_H
@@ -125,7 +125,7 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                double softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* Workspace bytes atw_decode needs: batch * h_q * num_splits * (head_dim + 2) * 4. */
+/* Workspace bytes atw_decode needs: batch * h_q * num_splits * (head_dim + 4) * 4. */
 size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits);
 
 /*

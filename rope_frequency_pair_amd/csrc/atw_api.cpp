@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/atw.h"
+#include "atw.h"
 #include "kernels.h"
 #include "planner.h"
 
@@ -147,9 +147,9 @@ int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, i
   if (plan_out == nullptr || pruned_out == nullptr) return fail(ATW_EINVAL, "output is NULL");
   if (n_q < 0 || n_kv < 0 || q_pos0 < 0 || tile_q <= 0 || tile_k <= 0)
     return fail(ATW_EINVAL, "sizes must be >= 0 and tiles > 0");
-  if (n_q * n_kv > (int64_t(1) << 40) || q_pos0 + n_q >= (int64_t(1) << 31) ||
-      n_kv >= (int64_t(1) << 31))
-    return fail(ATW_EINVAL, "n_q * n_kv must be <= 2^40 and positions < 2^31");
+  if (n_q * n_kv > (int64_t(1) << 40) || q_pos0 + n_q > (int64_t(1) << 30) ||
+      n_kv > (int64_t(1) << 30))
+    return fail(ATW_EINVAL, "n_q * n_kv must be <= 2^40 and positions < 2^30");
   atw::PlanParams p{};
   p.plan = plan_out;
   p.pruned = pruned_out;
@@ -178,8 +178,8 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
   if (dtype != ATW_F32 && dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "dtype must be ATW_F32 or ATW_BF16");
   if (batch <= 0 || n_q < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "batch > 0, n_q >= 0, q_pos0 >= 0 required");
   if (n_kv < 1) return fail(ATW_EINVAL, "n_kv must be >= 1");
-  if (q_pos0 + n_q >= (int64_t(1) << 31) || n_kv >= (int64_t(1) << 31))
-    return fail(ATW_EUNSUPPORTED, "positions must be < 2^31");
+  if (q_pos0 + n_q > (int64_t(1) << 30) || n_kv > (int64_t(1) << 30))
+    return fail(ATW_EUNSUPPORTED, "positions must be < 2^30");
   if (!std::isfinite(softmax_scale)) return fail(ATW_EINVAL, "softmax_scale must be finite");
   int16_t kvh[atw::kMaxHeadsQ];
   if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
@@ -213,9 +213,17 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
   p.h_q = h_q;
   p.causal = causal != 0;
   p.n_qblk = (int32_t)n_qblk;
+  p.n_kv_heads = h_kv;
   const double scale = softmax_scale > 0 ? softmax_scale : 1.0 / std::sqrt((double)head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
-  for (int h = 0; h < h_q; ++h) p.kvh[h] = kvh[h];
+  // query heads grouped by kv head: workgroups of one kv head share an XCD
+  int n = 0;
+  for (int kv = 0; kv < h_kv; ++kv) {
+    p.kv_first[kv] = (int16_t)n;
+    for (int h = 0; h < h_q; ++h)
+      if (kvh[h] == kv) p.qh_of_kv[n++] = (int16_t)h;
+  }
+  p.kv_first[h_kv] = (int16_t)n;
   fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
   return hip_status(atw::launch_prefill(p, dtype, head_dim, (hipStream_t)stream), "prefill launch");
 }
@@ -242,9 +250,9 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (!std::isfinite(softmax_scale)) return fail(ATW_EINVAL, "softmax_scale must be finite");
   if (kv_len == nullptr || q_pos == nullptr) return fail(ATW_EINVAL, "kv_len and q_pos must be non-NULL");
   for (int64_t b = 0; b < batch; ++b) {
-    if (kv_len[b] < 1 || kv_len[b] >= (int64_t(1) << 31))
-      return fail(ATW_EINVAL, "kv_len[%lld] = %lld must be in 1..2^31-1", (long long)b, (long long)kv_len[b]);
-    if (q_pos[b] < 0 || q_pos[b] >= (int64_t(1) << 31))
+    if (kv_len[b] < 1 || kv_len[b] > (int64_t(1) << 30))
+      return fail(ATW_EINVAL, "kv_len[%lld] = %lld must be in 1..2^30", (long long)b, (long long)kv_len[b]);
+    if (q_pos[b] < 0 || q_pos[b] >= (int64_t(1) << 30))
       return fail(ATW_EINVAL, "q_pos[%lld] out of range", (long long)b);
     if (causal && q_pos[b] < kv_len[b] - 1)
       return fail(ATW_EINVAL, "causal decode needs q_pos[%lld] >= kv_len - 1", (long long)b);

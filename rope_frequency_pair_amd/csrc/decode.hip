@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
       auto drop_cells = [&](int pp) {
         int thr_lo, thr_hi;
-        drop_bounds(qpos, p.win.w[pp], kbl, causal, kTK, &thr_lo, &thr_hi);
+        drop_bounds((int)qpos, p.win.w[pp], (int)kbl, causal, kTK, &thr_lo, &thr_hi);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int ko = acc_row(v);
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       // keys past the end of the split / not visible
       if (m_lo + kTK > k_end || (causal && m_lo + kTK - 1 > qpos)) {
         int thc, thr;
-        hide_bounds(qpos, kbl, k_end, causal, kTK, &thc, &thr);
+        hide_bounds((int)qpos, (int)kbl, k_end, causal, kTK, &thc, &thr);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int ko = acc_row(v);
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_swap_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
       if (__any(grow)) {
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   }
 
   // partial result of this split: [m (raw score units), l, -, -, o[D]] per query head
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   if (l32 < G) {
     const int qh = p.qh_of_kv[g0 + l32];
     float* w = p.ws + (((int64_t)b * p.h_q + qh) * p.splits + split) * (D + 4);

@@ -28,13 +28,36 @@ struct WindowArgs {
   double phi[kMaxPairs];    // theta_r / (2*pi)
 };
 
+// sin and cos of 2*pi*t for |t| <= 1/2 turn.  Quarter-turn reduction
+// (exact: t - q/4 with q = rint(4t)), then the Taylor series of sin to a^9
+// and cos to a^10 on |a| <= pi/4 (truncation below 2e-11), then the quadrant.
+__device__ __forceinline__ void sincos_turns(float t, float* s, float* c) {
+  const float q = __builtin_rintf(4.0f * t);
+  const float r = __builtin_fmaf(q, -0.25f, t);
+  const float a = r * 6.28318530717958648f;
+  const float a2 = a * a;
+  float sp = __builtin_fmaf(a2, 2.75573192239858907e-6f, -1.98412698412698413e-4f);
+  sp = __builtin_fmaf(a2, sp, 8.33333333333333333e-3f);
+  sp = __builtin_fmaf(a2, sp, -1.66666666666666667e-1f);
+  sp = __builtin_fmaf(a2, sp, 1.0f);
+  const float sa = a * sp;
+  float cp = __builtin_fmaf(a2, -2.75573192239858907e-7f, 2.48015873015873016e-5f);
+  cp = __builtin_fmaf(a2, cp, -1.38888888888888889e-3f);
+  cp = __builtin_fmaf(a2, cp, 4.16666666666666667e-2f);
+  cp = __builtin_fmaf(a2, cp, -0.5f);
+  const float ca = __builtin_fmaf(a2, cp, 1.0f);
+  const int qi = ((int)q) & 3;   // angle = a + qi * pi/2
+  const float s0 = (qi & 1) ? ca : sa, c0 = (qi & 1) ? sa : ca;
+  *s = (qi & 2) ? -s0 : s0;
+  *c = ((qi + 1) & 2) ? -c0 : c0;
+}
+
 // Accurate sin/cos of the RoPE angle pos * theta_r: the phase in turns is
-// formed and reduced to [-1/2, 1/2] in double, then sincosf on |angle| <= pi.
+// formed and reduced to [-1/2, 1/2] in double, then sincos_turns.
 __device__ __forceinline__ void rope_sincos(int64_t pos, double phi, float* s, float* c) {
   double t = (double)pos * phi;
   t -= __builtin_rint(t);
-  const float a = (float)(t * 6.283185307179586);
-  sincosf(a, s, c);
+  sincos_turns((float)t, s, c);
 }
 
 // Number of pairs whose window is shorter than delta, computed by one wave:
@@ -77,25 +100,34 @@ __device__ __forceinline__ bool pair_dropped(int64_t n, int64_t m, int wp, bool 
 // position kbase (ko in [0, span)).  For the query at position npos and a
 // partially windowed pair with window wp, the pair's term is dropped at the
 // cell iff ko < *lo || ko > *hi.  (Causal: distance npos - m > wp; non-causal:
-// |npos - m| > wp.)  Thresholds are clamped to [-1, span].
-__device__ __forceinline__ void drop_bounds(int64_t npos, int wp, int64_t kbase, bool causal,
-                                            int span, int* lo, int* hi) {
-  const int64_t l = npos - (int64_t)wp - kbase;
-  *lo = (int)max((int64_t)-1, min(l, (int64_t)span));
+// |npos - m| > wp.)  Positions are below 2^30, so with wp <= 2^31 - 1 every
+// difference taken on the selected branch fits in int32; thresholds saturate
+// to [-1, span].
+__device__ __forceinline__ void drop_bounds(int npos, int wp, int kbase, bool causal, int span,
+                                            int* lo, int* hi) {
+  const int d0 = npos - kbase;                 // key offset of the query position
+  *lo = (wp > d0) ? -1 : min(d0 - wp, span);
   *hi = span;
-  if (!causal) {
-    const int64_t h = npos + (int64_t)wp - kbase;
-    *hi = (int)max((int64_t)-1, min(h, (int64_t)span));
-  }
+  if (!causal) *hi = (wp >= span - d0) ? span : max(d0 + wp, -1);
 }
 
 // Visibility of the cell at key offset ko: hidden iff ko > *fut (a key after
 // the query, causal) or ko >= *end (past the last key n_end - 1).
-__device__ __forceinline__ void hide_bounds(int64_t npos, int64_t kbase, int64_t n_end, bool causal,
-                                            int span, int* fut, int* end) {
-  const int64_t c = causal ? npos - kbase : (int64_t)span;
-  *fut = (int)max((int64_t)-1, min(c, (int64_t)span));
-  *end = (int)max((int64_t)0, min(n_end - kbase, (int64_t)span));
+__device__ __forceinline__ void hide_bounds(int npos, int kbase, int n_end, bool causal, int span,
+                                            int* fut, int* end) {
+  *fut = causal ? max(-1, min(npos - kbase, span)) : span;
+  *end = max(0, min(n_end - kbase, span));
+}
+
+// Both lanes l and l^32 get f(x_l, x_{l^32}) for a symmetric f: the swap puts
+// the other half's value beside each lane's own.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -23,9 +23,10 @@ struct PrefillParams {
   void* o;
   int64_t qs[3], ks[3], vs[3], os[3];   // element strides (batch, head, token)
   int32_t batch, n_q, n_kv, q_pos0;
-  int32_t h_q, causal, n_qblk, pad0;
+  int32_t h_q, causal, n_qblk, n_kv_heads;
   float scale_log2;                      // softmax scale * log2(e)
-  int16_t kvh[kMaxHeadsQ];               // kv head of each query head
+  int16_t qh_of_kv[kMaxHeadsQ];          // query heads grouped by kv head (kv-major)
+  int16_t kv_first[kMaxHeadsQ + 1];      // start of each kv head's group in qh_of_kv
   WindowArgs win;
 };
 

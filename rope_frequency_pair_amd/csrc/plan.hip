@@ -36,12 +36,12 @@ __global__ __launch_bounds__(64) void plan_kernel(const PlanParams p) {
         const int64_t n = n_lo + cell / cols;
         const int ko = (int)(cell % cols);
         int fut, end;
-        hide_bounds(n, m_lo, n_end, p.causal != 0, p.tile_k, &fut, &end);
+        hide_bounds((int)n, (int)m_lo, (int)n_end, p.causal != 0, p.tile_k, &fut, &end);
         if (ko > fut || ko >= end) continue;            // not a visible cell
         int c = r_any;                                   // pairs below r_any: never computed
         for (int pp = r_any; pp < r_full; ++pp) {
           int lo, hi;
-          drop_bounds(n, p.win.w[pp], m_lo, p.causal != 0, p.tile_k, &lo, &hi);
+          drop_bounds((int)n, p.win.w[pp], (int)m_lo, p.causal != 0, p.tile_k, &lo, &hi);
           if (ko < lo || ko > hi) ++c;
         }
         cnt += c;

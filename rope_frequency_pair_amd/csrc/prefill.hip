@@ -11,13 +11,17 @@
 // Layout of the work (designed for CDNA4, not taken from the pages):
 //  * one workgroup = 8 waves = 256 consecutive query rows of one query head;
 //    a wave owns 32 rows; key tiles of 64 keys, double-buffered in LDS;
+//  * workgroups are dispatched largest causal blocks first, and the ones
+//    resident on one XCD (workgroup i runs on XCD i mod 8) are consecutive
+//    blocks of one (batch, kv head), so they share key/value tiles in its L2
+//    (whole kv heads per XCD when they divide evenly, else balanced rounds);
 //  * scores are computed transposed, S^T = K' Q'^T, with
 //    v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2f32), so each
 //    lane holds 16 keys of one query column and the row max / sum are mostly
 //    in-lane; lanes l and l+32 share a query;
-//  * the contraction axis is ordered pair by pair ((r, r+h) adjacent,
-//    "frequency-ordered"): one bf16 k-step of 16 covers 8 whole pairs, so the
-//    retained pairs [r, h) are a contiguous range of k-steps;
+//  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
+//    bf16 k-step of 16 covers 8 whole pairs, so the retained pairs [r, h) are
+//    a contiguous range of k-steps;
 //  * pairs that are in the window for some cells of a wave's tile and not for
 //    others ("partial" pairs) are added first, one pair per MFMA, and after
 //    each such pair the cells beyond its window are reset to zero; because
@@ -26,6 +30,10 @@
 //  * O^T += V^T P^T with P^T taken straight from the S^T registers; V is
 //    transposed into LDS (keys contiguous per head-dim row, in the key order
 //    the S^T register layout produces);
+//  * waves 0-3 run each tile as [QK^T, softmax, PV, RoPE staging of the
+//    next tile] and waves 4-7 as [staging, QK^T, softmax, PV], so on each
+//    SIMD the MFMA stretches of one wave meet the VALU stretches of the
+//    other; one workgroup barrier per tile;
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
 #include "device_common.h"
@@ -45,55 +53,122 @@ template <typename T, int D>
 struct Cfg {
   static constexpr int H = D / 2;
   static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int EPC = 16 / (int)sizeof(T);            // elements per 16-byte chunk
-  static constexpr int NCH = H / EPC;                         // chunks per half row
-  static constexpr int NK_TASKS = kTK * NCH;                  // K staging tasks per tile
-  static constexpr int KT = (NK_TASKS + kThreads - 1) / kThreads;
-  static constexpr int NV_TASKS = kBf16 ? 32 * (D / 8) : kTK * (D / 4);
-  static constexpr int VT = (NV_TASKS + kThreads - 1) / kThreads;
-  static constexpr int KROW = D + 16 / (int)sizeof(T);        // K' row (elements), 16 B pad
-  static constexpr int VROWS = kBf16 ? D : kTK;               // bf16: V^T rows; fp32: V rows
-  static constexpr int VROW = kBf16 ? (kTK + 8) : (D + 4);
-  static constexpr int NKS = kBf16 ? D / 16 : H;              // QK^T k-steps
-  static constexpr int ND = D / 32;                           // 32-wide head-dim blocks
+  // K staging: thread = (key tid/8, pair group tid%8) of PPT pairs
+  static constexpr int PPT = H / 8;
+  // bf16 K' row: 16-byte quads of 4 pairs; quad qd is stored at unit
+  // (qd % 2) * (H/8) + qd / 2, so the two quads of a k-step live in two
+  // half-row regions and the staging writes of one key are contiguous
+  static constexpr int KROW = D + 16 / (int)sizeof(T);     // elements, 16 B pad
+  // V [64 keys][VROW], row-major as in memory.  bf16 rows are padded so the
+  // row stride is 16 or 48 dwords modulo 64: the transposing reads of four
+  // consecutive rows then hit disjoint banks.  fp32: 4-element pad.
+  static constexpr int VROW = kBf16 ? (D == 128 ? 160 : 96) : (D + 4);
+  static constexpr int NVT = D * (int)sizeof(T) / 128;      // 16-byte V chunks per thread per tile
+  static constexpr int NKS = kBf16 ? D / 16 : H;            // QK^T k-steps
+  static constexpr int ND = D / 32;                         // 32-wide head-dim blocks
 };
 
 template <typename T, int D>
 struct Smem {
   T k[2][kTK][Cfg<T, D>::KROW];
-  T v[2][Cfg<T, D>::VROWS][Cfg<T, D>::VROW];
-  float2 step[D / 2];
+  T v[2][kTK][Cfg<T, D>::VROW];
 };
 
 __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// Key offset (within a 32-key block) of accumulator register v in lane half s
-// for the 32x32 MFMA output layout.
+// Key offset (within a 32-key block, before + 4*s) of accumulator register v
+// in the 32x32 MFMA output layout.
 __device__ __forceinline__ constexpr int acc_row(int v) { return 8 * (v >> 2) + (v & 3); }
 
-template <typename T>
-__device__ __forceinline__ u32x4 load16(const T* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8 bytes addressed by lanes i/4, i/4+4, i/4+8, i/4+12 (in that order).
+__device__ __forceinline__ v4i16 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<void*>(p));
+}
+
+// Register chunks of 8, 16 or 32 bytes.
+template <int BYTES>
+struct Chunk {
+  static constexpr int N = BYTES / 4;
+  uint32_t w[N];
+};
+template <int BYTES>
+__device__ __forceinline__ Chunk<BYTES> load_chunk(const void* p) {
+  Chunk<BYTES> c;
+  if constexpr (BYTES == 8) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    c.w[0] = x[0];
+    c.w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(p)[i];
+      c.w[4 * i] = x[0];
+      c.w[4 * i + 1] = x[1];
+      c.w[4 * i + 2] = x[2];
+      c.w[4 * i + 3] = x[3];
+    }
+  }
+  return c;
+}
+template <int BYTES>
+__device__ __forceinline__ Chunk<BYTES> zero_chunk() {
+  Chunk<BYTES> c;
+#pragma unroll
+  for (int i = 0; i < BYTES / 4; ++i) c.w[i] = 0u;
+  return c;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParams p) {
   using C = Cfg<T, D>;
   constexpr int H = C::H;
-  constexpr int EPC = C::EPC;
+  constexpr int PPT = C::PPT;
+  constexpr int KBYTES = PPT * (int)sizeof(T);                 // bytes per half row per K task
   __shared__ Smem<T, D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sh = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;   // 0: waves 0-3, 1: waves 4-7 (one phase later)
 
-  // ---- work item: largest causal blocks first
-  const int per_qb = p.h_q * p.batch;
-  const int qb = p.n_qblk - 1 - (int)(blockIdx.x / per_qb);
-  const int rem = (int)(blockIdx.x % per_qb);
-  const int hq = rem % p.h_q, bb = rem / p.h_q;
-  const int kvh = p.kvh[hq];
+  // ---- work item.  The list (batch, kv head, query block descending, query
+  // head) is mapped onto the XCDs (XCD x runs workgroups x, x+8, ...):
+  //  * when the (batch, kv head) groups split evenly over the 8 XCDs, XCD x
+  //    takes a contiguous eighth of the list (whole groups: its L2 serves
+  //    only its own kv heads);
+  //  * otherwise the list is dealt in rounds of 8 x 32 entries, XCD x taking
+  //    32 consecutive entries per round, which balances the causal work;
+  // the last partial round keeps the identity order.
+  int bb, hq, qb, kvh;
+  {
+    constexpr int kRound = 32;
+    const int W = p.n_qblk * p.h_q * p.batch;
+    const int idx = (int)blockIdx.x, x = idx & 7, li = idx >> 3;
+    int pos;
+    if ((p.batch * p.n_kv_heads) % 8 == 0 && W % 8 == 0) {
+      pos = x * (W >> 3) + li;
+    } else {
+      const int full = W / (8 * kRound);
+      const int round = li / kRound;
+      pos = (round < full) ? round * 8 * kRound + x * kRound + li % kRound : idx;
+    }
+    const int per_b = p.n_qblk * p.h_q;
+    bb = pos / per_b;
+    const int r = pos - bb * per_b;
+    int j = 0;
+    while ((int)p.kv_first[j + 1] * p.n_qblk <= r) ++j;
+    const int r2 = r - (int)p.kv_first[j] * p.n_qblk;
+    const int G = p.kv_first[j + 1] - p.kv_first[j];
+    qb = p.n_qblk - 1 - r2 / G;
+    hq = p.qh_of_kv[p.kv_first[j] + r2 % G];
+    kvh = j;
+  }
 
   const T* qbase = (const T*)p.q + bb * p.qs[0] + hq * p.qs[1];
   const T* kbase = (const T*)p.k + bb * p.ks[0] + kvh * p.ks[1];
@@ -101,22 +176,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
   T* obase = (T*)p.o + bb * p.os[0] + hq * p.os[1];
 
   const bool causal = p.causal != 0;
+  const int n_kv = p.n_kv;
   const int i0 = qb * kPrefillBlockRows;
   const int g_last = min(i0 + kPrefillBlockRows - 1, p.n_q - 1);
   const int w_first = i0 + wave * kRowsW;
   const int w_last = min(w_first + kRowsW - 1, p.n_q - 1);
   const bool wave_rows = w_first <= w_last;
-  const int64_t n_lo = (int64_t)p.q_pos0 + w_first, n_hi = (int64_t)p.q_pos0 + w_last;
-  const int64_t gn_lo = (int64_t)p.q_pos0 + i0, gn_hi = (int64_t)p.q_pos0 + g_last;
+  const int n_lo = p.q_pos0 + w_first, n_hi = p.q_pos0 + w_last;
+  const int gn_lo = p.q_pos0 + i0, gn_hi = p.q_pos0 + g_last;
   const int qrow = min(w_first + l32, p.n_q - 1);
-  const int64_t npos = (int64_t)p.q_pos0 + qrow;
+  const int npos = p.q_pos0 + qrow;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
-
-  if (tid < H) {
-    float s, c;
-    rope_sincos(kTK, p.win.phi[tid], &s, &c);
-    sm.step[tid] = make_float2(c, s);
-  }
 
   // ---- query: load, rotate at its position, keep as MFMA operand
   const T* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
@@ -154,174 +224,171 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
   for (int b = 0; b < C::ND; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int64_t kv_end = causal ? min((int64_t)p.n_kv, gn_hi + 1) : (int64_t)p.n_kv;
-  const int n_kt = (int)((kv_end + kTK - 1) / kTK);
+  const int kv_end = causal ? min(n_kv, gn_hi + 1) : n_kv;
+  const int n_kt = (kv_end + kTK - 1) / kTK;
 
-  // ---- staging tasks of this thread (fixed over tiles)
-  int kj[C::KT], kc[C::KT];
-  bool kon[C::KT];
-#pragma unroll
-  for (int i = 0; i < C::KT; ++i) {
-    const int task = tid + i * kThreads;
-    kon[i] = task < C::NK_TASKS;
-    kj[i] = kon[i] ? task / C::NCH : 0;
-    kc[i] = kon[i] ? task % C::NCH : 0;
+  // ---- staging tasks (fixed over tiles)
+  // K: wave w stages pair chunk kc (PPT pairs) of all 64 keys of a tile, lane =
+  // key, so a chunk that the window prunes is skipped by a whole wave; chunks
+  // are interleaved between the two wave groups to keep them balanced.
+  const int kj = lane, kc = ((wave & 3) << 1) | (wave >> 2);
+  const T* ksrc = kbase + (int64_t)kj * p.ks[2] + kc * PPT;
+  const int64_t kstep = (int64_t)kTK * p.ks[2];
+  int koff0, koff1;                              // LDS element offsets of the K' writes
+  if constexpr (C::kBf16) {
+    if constexpr (PPT == 8) {
+      koff0 = kj * C::KROW + 8 * kc;             // quad 2kc   -> unit kc
+      koff1 = kj * C::KROW + 8 * (H / 8 + kc);   // quad 2kc+1 -> unit H/8 + kc
+    } else {                                     // PPT == 4: quad kc
+      koff0 = kj * C::KROW + 8 * ((kc & 1) * (H / 8) + (kc >> 1));
+      koff1 = koff0;
+    }
+  } else {
+    koff0 = kj * C::KROW + 2 * kc * PPT;         // fp32: pairs interleaved
+    koff1 = koff0;
   }
-  int vtask[C::VT];
-  bool von[C::VT];
+  // RoPE step over one key tile (64*theta_r) for the wave's pairs: uniform
+  float st_c[PPT], st_s[PPT];
 #pragma unroll
-  for (int i = 0; i < C::VT; ++i) {
-    // when there are fewer V tasks than threads, give them to the threads
-    // with the fewest K tasks (the last ones)
-    const int t = C::NV_TASKS < kThreads ? (tid + kThreads - C::NV_TASKS) % kThreads : tid;
-    vtask[i] = t + i * kThreads;
-    von[i] = vtask[i] < C::NV_TASKS;
+  for (int e = 0; e < PPT; ++e) {
+    float s, c;
+    rope_sincos(kTK, p.win.phi[kc * PPT + e], &s, &c);
+    st_c[e] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
+    st_s[e] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s)));
   }
-  float rc[C::KT][EPC], rs[C::KT][EPC];   // cos/sin at the next staged tile
-  u32x4 kreg[C::KT][2];
-  u32x4 vreg[C::VT][C::kBf16 ? 2 : 1];
+  // V: row-major 16-byte chunks, task = tid + 512*i -> (key, chunk)
+  constexpr int VCH = D * (int)sizeof(T) / 16;   // 16-byte chunks per V row
+  const T* vsrc[C::NVT];
+  int voff[C::NVT], vkey[C::NVT];
+#pragma unroll
+  for (int i = 0; i < C::NVT; ++i) {
+    const int task = tid + kThreads * i;
+    vkey[i] = task / VCH;
+    const int ch = task % VCH;
+    vsrc[i] = vbase + (int64_t)vkey[i] * p.vs[2] + ch * (16 / (int)sizeof(T));
+    voff[i] = vkey[i] * C::VROW + ch * (16 / (int)sizeof(T));
+  }
+  const int64_t vstep = (int64_t)kTK * p.vs[2];
 
-  // WG-wide first pair needed in tile t (the staging start)
+  float rc[PPT], rs[PPT];          // cos/sin of the RoPE angle of the next staged K tile
+  Chunk<KBYTES> kreg0, kreg1;
+  Chunk<16> vreg[C::NVT];
+
+  // WG-wide first pair needed in key tile t (the staging start)
   auto stage_lo = [&](int t) -> int {
-    const int64_t m_lo = (int64_t)t * kTK;
-    const int64_t m_hi = min(m_lo + kTK - 1, (int64_t)p.n_kv - 1);
+    const int m_lo = t * kTK;
+    const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
     int64_t dmin = 0, dmax = 0;
     if (!tile_distance_range(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return H;
     const int r = wave_pairs_below(w_lane, dmin);
     return C::kBf16 ? (r & ~7) : r;
   };
 
-  auto stage_load = [&](int t, int rlo) {
-#pragma unroll
-    for (int i = 0; i < C::KT; ++i) {
-      const int64_t m = (int64_t)t * kTK + kj[i];
-      const bool need = kon[i] && (kc[i] + 1) * EPC > rlo && m < p.n_kv;
-      if (need) {
-        const T* src = kbase + m * p.ks[2] + kc[i] * EPC;
-        kreg[i][0] = load16(src);
-        kreg[i][1] = load16(src + H);
+  auto load_k = [&](int t) {
+    const int m = t * kTK + kj;
+    if ((kc + 1) * PPT > stage_lo(t)) {          // uniform over the wave
+      if (m < n_kv) {
+        const T* src = ksrc + t * kstep;
+        kreg0 = load_chunk<KBYTES>(src);
+        kreg1 = load_chunk<KBYTES>(src + H);
       } else {
-        kreg[i][0] = u32x4{0, 0, 0, 0};
-        kreg[i][1] = u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::VT; ++i) {
-      if constexpr (C::kBf16) {
-        const int pr = vtask[i] / (D / 8), dc = vtask[i] % (D / 8);
-        const int64_t m = (int64_t)t * kTK + 2 * pr;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          if (von[i] && m + e < p.n_kv)
-            vreg[i][e] = load16(vbase + (m + e) * p.vs[2] + dc * 8);
-          else
-            vreg[i][e] = u32x4{0, 0, 0, 0};
-        }
-      } else {
-        const int j = vtask[i] / (D / 4), dc = vtask[i] % (D / 4);
-        const int64_t m = (int64_t)t * kTK + j;
-        if (von[i] && m < p.n_kv)
-          vreg[i][0] = load16(vbase + m * p.vs[2] + dc * 4);
-        else
-          vreg[i][0] = u32x4{0, 0, 0, 0};
+        kreg0 = zero_chunk<KBYTES>();
+        kreg1 = zero_chunk<KBYTES>();
       }
     }
   };
-
-  auto stage_store = [&](int t, int buf, int rlo) {
+  auto load_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < C::KT; ++i) {
-      if (!kon[i]) continue;
-      const int64_t m = (int64_t)t * kTK + kj[i];
-      if (t % kReanchor == 0) {
+    for (int i = 0; i < C::NVT; ++i)
+      vreg[i] = (t * kTK + vkey[i] < n_kv) ? load_chunk<16>(vsrc[i] + t * vstep) : zero_chunk<16>();
+  };
+  auto write_k = [&](int t) {
+    const int m = t * kTK + kj;
+    if (t % kReanchor == 0) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) rope_sincos(m, p.win.phi[kc[i] * EPC + e], &rs[i][e], &rc[i][e]);
-      }
-      if ((kc[i] + 1) * EPC > rlo) {
-        T* dst = &sm.k[buf][kj[i]][2 * kc[i] * EPC];
-        if constexpr (C::kBf16) {
-          u32x4 o0, o1;
+      for (int e = 0; e < PPT; ++e) rope_sincos(m, p.win.phi[kc * PPT + e], &rs[e], &rc[e]);
+    }
+    if ((kc + 1) * PPT > stage_lo(t)) {          // uniform over the wave
+      T* dst = &sm.k[t & 1][0][0];
+      if constexpr (C::kBf16) {
+        uint32_t w[PPT];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
-            const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-            const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-            const uint32_t pk = pack_bf16(x1 * rc[i][e] - x2 * rs[i][e], x2 * rc[i][e] + x1 * rs[i][e]);
-            if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
-          }
-          reinterpret_cast<u32x4*>(dst)[0] = o0;
-          reinterpret_cast<u32x4*>(dst)[1] = o1;
-        } else {
-          f32x4 o0, o1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x1 = __uint_as_float(kreg[i][0][e]), x2 = __uint_as_float(kreg[i][1][e]);
-            const float y1 = x1 * rc[i][e] - x2 * rs[i][e], y2 = x2 * rc[i][e] + x1 * rs[i][e];
-            if (e < 2) { o0[2 * e] = y1; o0[2 * e + 1] = y2; }
-            else { o1[2 * e - 4] = y1; o1[2 * e - 3] = y2; }
-          }
-          reinterpret_cast<f32x4*>(dst)[0] = o0;
-          reinterpret_cast<f32x4*>(dst)[1] = o1;
+        for (int e = 0; e < PPT; ++e) {
+          const uint32_t wa = kreg0.w[e >> 1], wb = kreg1.w[e >> 1];
+          const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
+          const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+          w[e] = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
         }
-      }
-      // advance the rotation to the next tile's key position
+        *reinterpret_cast<u32x4*>(dst + koff0) = u32x4{w[0], w[1], w[2], w[3]};
+        if constexpr (PPT == 8) *reinterpret_cast<u32x4*>(dst + koff1) = u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+        float y[2 * PPT];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const float2 st = sm.step[kc[i] * EPC + e];
-        const float c = rc[i][e], s = rs[i][e];
-        rc[i][e] = c * st.x - s * st.y;
-        rs[i][e] = s * st.x + c * st.y;
+        for (int e = 0; e < PPT; ++e) {
+          const float x1 = __uint_as_float(kreg0.w[e]), x2 = __uint_as_float(kreg1.w[e]);
+          y[2 * e] = x1 * rc[e] - x2 * rs[e];
+          y[2 * e + 1] = x2 * rc[e] + x1 * rs[e];
+        }
+#pragma unroll
+        for (int i = 0; i < PPT / 2; ++i)
+          reinterpret_cast<f32x4*>(dst + koff0)[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
       }
     }
+    // advance the rotation to the next tile's key position
 #pragma unroll
-    for (int i = 0; i < C::VT; ++i) {
-      if (!von[i]) continue;
-      if constexpr (C::kBf16) {
-        const int pr = vtask[i] / (D / 8), dc = vtask[i] % (D / 8);
-        const int pos = swap_bits23(2 * pr);   // key order of the S^T register layout
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w0 = vreg[i][0][e >> 1], w1 = vreg[i][1][e >> 1];
-          const uint32_t pk = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                      : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-          const int row = dc * 8 + e;
-          const int unit = (pos >> 3) ^ ((row >> 3) & 7);
-          *reinterpret_cast<uint32_t*>(&sm.v[buf][row][unit * 8 + (pos & 7)]) = pk;
-        }
-      } else {
-        const int j = vtask[i] / (D / 4), dc = vtask[i] % (D / 4);
-        *reinterpret_cast<u32x4*>(&sm.v[buf][j][dc * 4]) = vreg[i][0];
-      }
+    for (int e = 0; e < PPT; ++e) {
+      const float c = rc[e], s = rs[e];
+      rc[e] = c * st_c[e] - s * st_s[e];
+      rs[e] = s * st_c[e] + c * st_s[e];
     }
   };
+  auto write_v = [&](int t) {
+    T* dst = &sm.v[t & 1][0][0];
+#pragma unroll
+    for (int i = 0; i < C::NVT; ++i)
+      *reinterpret_cast<u32x4*>(dst + voff[i]) = u32x4{vreg[i].w[0], vreg[i].w[1], vreg[i].w[2], vreg[i].w[3]};
+  };
 
-  __syncthreads();   // step table
-  {
-    const int rlo = stage_lo(0);
-    stage_load(0, rlo);
-    stage_store(0, 0, rlo);
+  // ---- prologue: tile 0 by everyone; waves 4-7 also load tile 1
+  load_k(0);
+  load_v(0);
+  write_k(0);
+  write_v(0);
+  if (grp == 1 && n_kt > 1) {
+    load_k(1);
+    load_v(1);
   }
   __syncthreads();
 
   for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    int rlo_next = H;
-    if (t + 1 < n_kt) {
-      rlo_next = stage_lo(t + 1);
-      stage_load(t + 1, rlo_next);
+    if (grp == 0) {
+      if (t + 1 < n_kt) {
+        load_k(t + 1);
+        load_v(t + 1);
+      }
+    } else {
+      if (t + 1 < n_kt) {
+        write_k(t + 1);
+        write_v(t + 1);
+      }
+      if (t + 2 < n_kt) {
+        load_k(t + 2);
+        load_v(t + 2);
+      }
     }
 
-    const int64_t m_lo = (int64_t)t * kTK;
-    const int64_t m_hi = min(m_lo + kTK - 1, (int64_t)p.n_kv - 1);
+    const int m_lo = t * kTK;
+    const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
     int64_t dmin = 0, dmax = 0;
     if (wave_rows && tile_distance_range(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
       const int r_any = wave_pairs_below(w_lane, dmin);
       const int r_full = wave_pairs_below(w_lane, dmax);
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      const int64_t kbase_lane = m_lo + 4 * sh;   // key position of acc row 0 in this lane half
+      const int kbase_lane = m_lo + 4 * sh;
+      f32x16 sacc[2];
+      const T* kt = &sm.k[t & 1][0][0];
 
-      // zero the cells where pair pp is outside its window
-      auto drop_cells = [&](int pp) {
+      // reset the cells of x beyond the window of partially windowed pair pp
+      auto drop_cells = [&](f32x16 (&x)[2], int pp) {
         int thr_lo, thr_hi;
         drop_bounds(npos, p.win.w[pp], kbase_lane, causal, kTK, &thr_lo, &thr_hi);
 #pragma unroll
@@ -329,67 +396,95 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int ko = 32 * blk + acc_row(v);
-            if (ko < thr_lo || ko > thr_hi) sacc[blk][v] = 0.f;
+            if (ko < thr_lo || ko > thr_hi) x[blk][v] = 0.f;
           }
       };
 
       if constexpr (C::kBf16) {
-        const T* krow0 = &sm.k[buf][l32][0];
-        const T* krow1 = &sm.k[buf][32 + l32][0];
+        const T* krow0 = kt + l32 * C::KROW + 8 * sh * (H / 8);
+        const T* krow1 = krow0 + 32 * C::KROW;
+        // pairs kept for every cell: k-steps kk0..NKS-1, taken from the top so
+        // the first MFMA starts from a zero accumulator; the operands of the
+        // next k-step are read from LDS while the current one multiplies
+        const int kk0 = r_full >> 3;
+        if (kk0 < C::NKS) {
+          bf16x8 na0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * (C::NKS - 1));
+          bf16x8 na1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * (C::NKS - 1));
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          const int p0 = 8 * ks;
-          if (p0 + 8 <= r_any) continue;
-          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow0 + 2 * (p0 + 4 * sh));
-          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow1 + 2 * (p0 + 4 * sh));
-          const u32x4 qw = __builtin_bit_cast(u32x4, qop[ks]);
-          const int plo = max(p0, r_any), phi_ = min(p0 + 8, r_full);
-          for (int pp = plo; pp < phi_; ++pp) {
-            const int u = pp - p0;
-            u32x4 bw = u32x4{0, 0, 0, 0};
-            if (sh == (u >> 2)) {
-              const int d = u & 3;
-              bw[0] = d == 0 ? qw[0] : 0u;
-              bw[1] = d == 1 ? qw[1] : 0u;
-              bw[2] = d == 2 ? qw[2] : 0u;
-              bw[3] = d == 3 ? qw[3] : 0u;
+          for (int ks = C::NKS - 1; ks >= 0; --ks) {
+            if (ks < kk0) break;
+            const bf16x8 a0 = na0, a1 = na1;
+            if (ks > kk0) {
+              na0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * (ks - 1));
+              na1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * (ks - 1));
             }
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
-            drop_cells(pp);
-          }
-          if (p0 + 8 > r_full) {
-            u32x4 bw = qw;
-            if (r_full > p0) {
+            u32x4 bw = __builtin_bit_cast(u32x4, qop[ks]);
+            if (ks == kk0 && (r_full & 7)) {   // pairs below r_full of this k-step are partial
 #pragma unroll
               for (int d = 0; d < 4; ++d)
-                if (p0 + 4 * sh + d < r_full) bw[d] = 0u;
+                if (8 * ks + 4 * sh + d < r_full) bw[d] = 0u;
             }
             const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
+            if (ks == C::NKS - 1) {
+              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, f32x16{}, 0, 0, 0);
+              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, f32x16{}, 0, 0, 0);
+            } else {
+              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
+              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
+            }
           }
+        } else {
+          sacc[0] = f32x16{};
+          sacc[1] = f32x16{};
+        }
+        // partially windowed pairs [r_any, r_full): one pair per MFMA into a
+        // separate accumulator, ascending, each followed by the reset
+        if (r_any < r_full) {
+          f32x16 x[2] = {f32x16{}, f32x16{}};
+          for (int pp = r_any; pp < r_full; ++pp) {
+            const int ks = pp >> 3, uu = pp & 7;
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * ks);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * ks);
+            uint32_t qd = 0u;
+#pragma unroll
+            for (int k2 = 0; k2 < C::NKS; ++k2) {
+              const u32x4 qw = __builtin_bit_cast(u32x4, qop[k2]);
+#pragma unroll
+              for (int d = 0; d < 4; ++d) qd = (k2 == ks && d == (uu & 3)) ? qw[d] : qd;
+            }
+            const bool mine = sh == (uu >> 2);
+            u32x4 bw;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+            x[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, x[0], 0, 0, 0);
+            x[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, x[1], 0, 0, 0);
+            drop_cells(x, pp);
+          }
+          sacc[0] += x[0];
+          sacc[1] += x[1];
         }
       } else {
-        const T* krow0 = &sm.k[buf][l32][0];
-        const T* krow1 = &sm.k[buf][32 + l32][0];
+        const T* krow0 = kt + l32 * C::KROW + sh;
+        const T* krow1 = krow0 + 32 * C::KROW;
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
 #pragma unroll
         for (int r = 0; r < H; ++r) {
           if (r < r_any) continue;
-          const float a0 = (float)krow0[2 * r + sh];
-          const float a1 = (float)krow1[2 * r + sh];
+          const float a0 = (float)krow0[2 * r];
+          const float a1 = (float)krow1[2 * r];
           sacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, qf[r], sacc[0], 0, 0, 0);
           sacc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, qf[r], sacc[1], 0, 0, 0);
-          if (r < r_full) drop_cells(r);
+          if (r < r_full) drop_cells(sacc, r);
         }
       }
 
       // causal and ragged-tail masks (cells outside the attended set)
-      const bool need_mask = (causal && m_lo + kTK - 1 > n_lo) || (m_lo + kTK > p.n_kv);
+      const bool need_mask = (causal && m_lo + kTK - 1 > n_lo) || (m_lo + kTK > n_kv);
       if (need_mask) {
         int thc, thr;
-        hide_bounds(npos, kbase_lane, p.n_kv, causal, kTK, &thc, &thr);
+        hide_bounds(npos, kbase_lane, n_kv, causal, kTK, &thc, &thr);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -399,13 +494,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
           }
       }
 
-      // online softmax (base-2, scale folded into the exponent)
+      // online softmax (base 2, scale folded into the exponent)
       float mx = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[blk][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_swap_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
       if (__any(grow)) {
@@ -417,57 +512,64 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
       }
       const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
       float lsum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][v], p.scale_log2, -mb));
-          sacc[blk][v] = e;
-          if constexpr (!C::kBf16) lsum += e;
-        }
-
-      // O^T += V^T P^T
+      const T* vt = &sm.v[t & 1][0][0];
       if constexpr (C::kBf16) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          // V operands of this key group first, so their LDS latency overlaps
+          // the exponentials below.  Transposing reads: lane l gets four keys
+          // of head-dim row 32b + l%32 (the keys of its S^T registers).
+          bf16x8 va[C::ND];
+#pragma unroll
+          for (int b = 0; b < C::ND; ++b) {
+            const T* base = vt + (16 * g + 4 * sh + ((lane & 15) >> 2)) * C::VROW + 32 * b +
+                            16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            const v4i16 lo = lds_read_tr16(base);
+            const v4i16 hi = lds_read_tr16(base + 8 * C::VROW);
+            va[b] = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          }
           u32x4 pw;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            pw[i] = pack_bf16(sacc[g >> 1][8 * (g & 1) + 2 * i], sacc[g >> 1][8 * (g & 1) + 2 * i + 1]);
+            const int v0 = 8 * (g & 1) + 2 * i;
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0], p.scale_log2, -mb));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0 + 1], p.scale_log2, -mb));
+            pw[i] = pack_bf16(e0, e1);
             // the normalizer sums the same rounded weights the PV product uses
             lsum = sum_bf16x2(pw[i], lsum);
           }
           const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-          for (int b = 0; b < C::ND; ++b) {
-            const int row = 32 * b + l32;
-            const int unit = (2 * g + sh) ^ ((row >> 3) & 7);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.v[buf][row][unit * 8]);
-            oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop, oacc[b], 0, 0, 0);
-          }
+          for (int b = 0; b < C::ND; ++b)
+            oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[b], pop, oacc[b], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][v], p.scale_log2, -mb));
+            lsum += e;
             const int key = 32 * blk + acc_row(v) + 4 * sh;
 #pragma unroll
             for (int b = 0; b < C::ND; ++b) {
-              const float a = (float)sm.v[buf][key][32 * b + l32];
-              oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[blk][v], oacc[b], 0, 0, 0);
+              const float a = (float)vt[key * C::VROW + 32 * b + l32];
+              oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, e, oacc[b], 0, 0, 0);
             }
           }
       }
       l_run += lsum;
     }
 
-    if (t + 1 < n_kt) stage_store(t + 1, buf ^ 1, rlo_next);
+    if (grp == 0 && t + 1 < n_kt) {
+      write_k(t + 1);
+      write_v(t + 1);
+    }
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = 1.f / l_tot;
   const int row = w_first + l32;
   if (wave_rows && row <= w_last) {
