@@ -69,6 +69,19 @@ def decode_bytes(atw, L, d, h_kv, batch, base, k_turns, window_on):
     return (k_bytes + v_bytes) * h_kv * batch, pruned / total
 
 
+def decode_line_bytes_banded(atw, L, q_pos, d, h_kv, batch, base, k_turns):
+    """HBM bytes one decode step must move at the memory system's 128-byte
+    line granularity with the pair-banded K cache (a line = one 8-pair band
+    of 4 consecutive keys, fetched if the band is in the window for any of
+    them) + all of V."""
+    import numpy as np
+    w = np.array(atw.window_widths(d, base, k_turns, True), dtype=np.int64)
+    first = np.arange(0, L, 4)                       # first key of each line
+    last = np.minimum(first + 3, L - 1)
+    lines = sum(int((q_pos - last <= w[8 * c + 7]).sum()) for c in range(d // 16))
+    return (lines * 128 + 2 * d * L) * h_kv * batch
+
+
 def time_launches(fn, stream, n):
     """Per-launch durations (ms) from HIP events recorded on the launch stream."""
     import torch
@@ -296,7 +309,36 @@ def main():
                                  "on_off_speedup": round(mb / ma, 3),
                                  "k_pair_terms_pruned": round(sh, 4),
                                  "bytes_on": by_on, "bytes_off": by_off}
-        del qd, kc, vc
+
+        # the same step over a pair-banded K cache (whole 128-byte lines pruned)
+        kb = atw.kcache_band(kc)
+        del kc
+        torch.cuda.synchronize()
+
+        def bstep(on):
+            atw.decode_banded(qd, kb, vc, [L] * wd.batch, [L] * wd.batch, rope_base=wd.rope_base,
+                              k_turns=wd.k_turns, window_on=on, num_splits=wd.splits, workspace=ws,
+                              out=od)
+
+        for _ in range(3):
+            bstep(True)
+            bstep(False)
+        a, b = [], []
+        for _ in range(10):
+            a += time_launches(lambda: bstep(True), stream, 1)
+            b += time_launches(lambda: bstep(False), stream, 1)
+        ma, mb = statistics.median(a), statistics.median(b)
+        by_line = decode_line_bytes_banded(atw, L, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base,
+                                           wd.k_turns)
+        result["decode_512k_banded"] = {
+            "ms_on": round(ma, 4), "ms_off": round(mb, 4),
+            "gbs_algorithmic_on": round(by_on / (ma * 1e-3) / 1e9, 1),
+            "hbm_frac_on": round(by_on / (ma * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gbs_line_bytes_on": round(by_line / (ma * 1e-3) / 1e9, 1),
+            "on_off_speedup": round(mb / ma, 3),
+            "on_vs_row_layout_off": round(result["decode_512k"]["ms_off"] / ma, 3),
+            "line_bytes_on": by_line}
+        del qd, kb, vc
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

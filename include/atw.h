@@ -114,7 +114,7 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
  *   workspace: device buffer of at least atw_decode_workspace_bytes(...)
  *           bytes for the per-split partial results (max, sum, unnormalised
  *           output); contents on entry are ignored.
- * batch <= 256.  dtype must be ATW_BF16.
+ * batch <= 256; at most 16 query heads per kv head.  dtype must be ATW_BF16.
  */
 int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
                int64_t batch, const int64_t* kv_len, const int64_t* q_pos,
@@ -127,6 +127,45 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
 
 /* Workspace bytes atw_decode needs: batch * h_q * num_splits * (head_dim + 4) * 4. */
 size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits);
+
+/*
+ * atw_decode_banded -- atw_decode over a pair-banded K cache.  The memory
+ * system of this GPU moves whole 128-byte lines; in the row layout every line
+ * of a key row holds dims of all pairs, so skipping the out-of-window pairs
+ * of a key ("The idea": the out-of-window prefix is never loaded) saves no
+ * memory traffic.  In the banded layout band c (c = 0 .. head_dim/16 - 1)
+ * holds, per key, dims [8c, 8c+8) followed by dims [h+8c, h+8c+8) (h =
+ * head_dim/2), i.e. rotation pairs 8c .. 8c+7, 32 bytes per key, keys
+ * contiguous:
+ *
+ *   k_bands [batch, h_kv, head_dim/16, L, 16]   k_strides[3] = element strides
+ *            of (batch, head, band); the token stride is 16 elements.
+ *
+ * A line then holds one band of 4 consecutive keys and is fetched only when
+ * the band is inside the window for one of them.  Every other argument, the
+ * result and the limits are those of atw_decode (bit-identical output for the
+ * same cache contents).
+ */
+int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, void* o,
+                      int32_t dtype, int64_t batch, const int64_t* kv_len, const int64_t* q_pos,
+                      int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                      const int64_t* q_strides, const int64_t* k_strides,
+                      const int64_t* v_strides, const int64_t* o_strides, double rope_base,
+                      double k_turns, int32_t causal, int32_t window_on, double softmax_scale,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * atw_kcache_band -- copy keys [t0, t0 + n_tokens) of a row-layout K cache
+ * (k_rows [batch, h_kv, L, head_dim], row_strides = (batch, head, token)) into
+ * a pair-banded one (k_bands as for atw_decode_banded, band_strides =
+ * (batch, head, band)).  Use it to band a whole cache or to append the keys
+ * of each new step.  The two buffers must not overlap.  dtype ATW_BF16,
+ * head_dim 64 or 128, t0 + n_tokens <= 2^30; n_tokens = 0 launches nothing.
+ * Asynchronous on stream.
+ */
+int atw_kcache_band(const void* k_rows, void* k_bands, int32_t dtype, int64_t batch, int32_t h_kv,
+                    int32_t head_dim, int64_t t0, int64_t n_tokens, const int64_t* row_strides,
+                    const int64_t* band_strides, void* stream);
 
 /*
  * atw_pruned_terms -- host only.  Number of pruned and total pair-terms

@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     UNBOUNDED,
     AtwError,
     decode,
+    decode_banded,
+    kcache_band,
     decode_workspace_bytes,
     default_scale,
     load_library,

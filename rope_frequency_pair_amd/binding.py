@@ -17,7 +17,8 @@ ATW_F32, ATW_BF16 = 0, 1
 UNBOUNDED = 1 << 62
 
 EXPORTED = [
-    "atw_prefill", "atw_decode", "atw_decode_workspace_bytes", "atw_pruned_terms",
+    "atw_prefill", "atw_decode", "atw_decode_banded", "atw_kcache_band",
+    "atw_decode_workspace_bytes", "atw_pruned_terms",
     "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
     "atw_version",
 ]
@@ -52,6 +53,10 @@ def load_library(path=LIB_PATH):
                                _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _i32, _vp,
                                ctypes.c_size_t, _vp]
     lib.atw_decode.restype = ctypes.c_int
+    lib.atw_decode_banded.argtypes = lib.atw_decode.argtypes
+    lib.atw_decode_banded.restype = ctypes.c_int
+    lib.atw_kcache_band.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _pi64, _pi64, _vp]
+    lib.atw_kcache_band.restype = ctypes.c_int
     lib.atw_decode_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
     lib.atw_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.atw_pruned_terms.argtypes = [_i64, _i64, _i64, _i32, _f64, _f64, _i32, _i32, _pi64, _pi64]
@@ -187,6 +192,47 @@ def decode(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=Tru
            scale=None, num_splits=64, kv_head_of_q=None, workspace=None, out=None, stream=None):
     """Windowed split-KV decode.  q [B, Hq, d]; caches [B, Hkv, L, d] bf16 CUDA
     tensors; kv_len, q_pos: per-sequence ints.  Returns out [B, Hq, d]."""
+    return _decode("atw_decode", q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal,
+                   window_on, scale, num_splits, kv_head_of_q, workspace, out, stream)
+
+
+def decode_banded(q, k_bands, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=True,
+                  window_on=True, scale=None, num_splits=64, kv_head_of_q=None, workspace=None,
+                  out=None, stream=None):
+    """decode() over a pair-banded K cache k_bands [B, Hkv, d/16, L, 16] (token
+    stride 16); v_cache [B, Hkv, L, d] as for decode()."""
+    if k_bands.dim() != 5 or k_bands.shape[-1] != 16 or k_bands.stride(3) != 16:
+        raise ValueError("k_bands must be [B, Hkv, d/16, L, 16] with token stride 16")
+    return _decode("atw_decode_banded", q, k_bands, v_cache, kv_len, q_pos, rope_base, k_turns,
+                   causal, window_on, scale, num_splits, kv_head_of_q, workspace, out, stream)
+
+
+def kcache_band(k_rows, k_bands=None, *, t0=0, n_tokens=None, stream=None):
+    """Copy keys [t0, t0 + n_tokens) of a row-layout K cache [B, Hkv, L, d] into
+    a pair-banded one [B, Hkv, d/16, L, 16] (allocated when k_bands is None).
+    Returns k_bands."""
+    import torch
+    lib = load_library()
+    B, Hkv, L, D = k_rows.shape
+    if k_bands is None:
+        k_bands = torch.empty((B, Hkv, D // 16, L, 16), dtype=k_rows.dtype, device=k_rows.device)
+    if k_bands.dim() != 5 or k_bands.shape[-1] != 16 or k_bands.stride(3) != 16:
+        raise ValueError("k_bands must be [B, Hkv, d/16, L, 16] with token stride 16")
+    if tuple(k_bands.shape[:3]) != (B, Hkv, D // 16) or k_bands.stride(4) != 1:
+        raise ValueError("k_bands shape does not match k_rows")
+    if n_tokens is None:
+        n_tokens = L - t0
+    if t0 < 0 or n_tokens < 0 or t0 + n_tokens > min(L, k_bands.shape[3]):
+        raise ValueError("token range outside the caches")
+    _check(lib.atw_kcache_band(
+        ctypes.c_void_p(k_rows.data_ptr()), ctypes.c_void_p(k_bands.data_ptr()),
+        _dtype_code(k_rows), B, Hkv, D, int(t0), int(n_tokens), _arr64(k_rows.stride()[:3]),
+        _arr64(k_bands.stride()[:3]), _stream_ptr(stream)))
+    return k_bands
+
+
+def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal, window_on,
+            scale, num_splits, kv_head_of_q, workspace, out, stream):
     import torch
     lib = load_library()
     B, Hq, D = q.shape
@@ -198,7 +244,7 @@ def decode(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=Tru
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
     q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
-    _check(lib.atw_decode(
+    _check(getattr(lib, entry)(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
         ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,

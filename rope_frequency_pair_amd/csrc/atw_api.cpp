@@ -233,13 +233,16 @@ size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, 
   return (size_t)batch * (size_t)h_q * (size_t)num_splits * (size_t)(head_dim + 4) * sizeof(float);
 }
 
-int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
-               int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
-               int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
-               const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
-               const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
-               int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
-               size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared body of atw_decode (row-layout K cache) and atw_decode_banded.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
+                int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
+                size_t workspace_bytes, void* stream, bool banded) {
   if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "decode supports head_dim 64 and 128 (got %d)", head_dim);
@@ -297,7 +300,7 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
     p.kv_len[b] = (int32_t)kv_len[b];
     p.q_pos[b] = (int32_t)q_pos[b];
   }
-  // group query heads by kv head; a kv head may serve at most 32 query heads
+  // group query heads by kv head; a kv head may serve at most 16 query heads
   int n = 0;
   for (int kv = 0; kv < h_kv; ++kv) {
     p.kv_first[kv] = (int16_t)n;
@@ -307,12 +310,70 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
         p.qh_of_kv[n++] = (int16_t)h;
         ++cnt;
       }
-    if (cnt > 32) return fail(ATW_EUNSUPPORTED, "decode supports at most 32 query heads per kv head");
+    if (cnt > 16) return fail(ATW_EUNSUPPORTED, "decode supports at most 16 query heads per kv head");
   }
   p.kv_first[h_kv] = (int16_t)n;
   p.group = h_q / h_kv;
   fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
-  return hip_status(atw::launch_decode(p, head_dim, (hipStream_t)stream), "decode launch");
+  return hip_status(atw::launch_decode(p, head_dim, banded, (hipStream_t)stream), "decode launch");
+}
+
+}  // namespace
+
+int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+               int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+               int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+               const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+               const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
+               int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rope_base, k_turns,
+                     causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
+                     stream, false);
+}
+
+int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, void* o,
+                      int32_t dtype, int64_t batch, const int64_t* kv_len, const int64_t* q_pos,
+                      int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                      const int64_t* q_strides, const int64_t* k_strides,
+                      const int64_t* v_strides, const int64_t* o_strides, double rope_base,
+                      double k_turns, int32_t causal, int32_t window_on, double softmax_scale,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_bands, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rope_base, k_turns,
+                     causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
+                     stream, true);
+}
+
+int atw_kcache_band(const void* k_rows, void* k_bands, int32_t dtype, int64_t batch, int32_t h_kv,
+                    int32_t head_dim, int64_t t0, int64_t n_tokens, const int64_t* row_strides,
+                    const int64_t* band_strides, void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ATW_EUNSUPPORTED, "banding supports head_dim 64 and 128 (got %d)", head_dim);
+  if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "banding supports dtype ATW_BF16 only");
+  if (batch < 1 || batch > 65535) return fail(ATW_EINVAL, "batch must be in 1..65535");
+  if (h_kv < 1 || h_kv > 65535) return fail(ATW_EINVAL, "h_kv must be in 1..65535");
+  if (t0 < 0 || n_tokens < 0 || t0 + n_tokens > (int64_t(1) << 30))
+    return fail(ATW_EINVAL, "token range [t0, t0 + n_tokens) must lie in [0, 2^30)");
+  if (n_tokens == 0) return ok();
+  if (!k_rows || !k_bands) return fail(ATW_EINVAL, "k_rows and k_bands must be non-NULL");
+  if (!aligned16(k_rows) || !aligned16(k_bands))
+    return fail(ATW_EUNSUPPORTED, "k_rows and k_bands must be 16-byte aligned");
+  if (int e = check_strides("row", row_strides, 3, 2)) return e;
+  if (int e = check_strides("band", band_strides, 3, 2)) return e;
+  atw::BandParams p{};
+  p.rows = k_rows;
+  p.bands = k_bands;
+  for (int i = 0; i < 3; ++i) {
+    p.rs[i] = row_strides[i];
+    p.bs[i] = band_strides[i];
+  }
+  p.t0 = t0;
+  p.n = n_tokens;
+  p.batch = (int32_t)batch;
+  p.h_kv = h_kv;
+  return hip_status(atw::launch_kcache_band(p, head_dim, (hipStream_t)stream), "banding launch");
 }
 
 }  // extern "C"

@@ -3,21 +3,27 @@
 // Method: "ATFlash — Per-RoPE-Wavelength Attention Windows", README, "The
 // idea": for a key at distance delta from the query, the pairs whose window
 // is shorter than delta contribute nothing, so that prefix of the pre-RoPE
-// key row is not loaded; the rest is rotated as it is loaded.  The
-// split-KV partition and the merge of per-split (max, sum, output) partials
-// are the standard online-softmax merge; the window does not change them.
+// key row is not loaded; the rest is rotated as it is loaded.  The split-KV
+// partition and the merge of per-split (max, sum, output) partials are the
+// standard online-softmax merge; the window does not change them.
 //
 // Work layout (CDNA4 design):
 //  * one workgroup = one wave = one (sequence, kv head, split); the columns
-//    of S^T = K' Q'^T are the query heads that read this kv head (GQA), so the
-//    key tile is read once for all of them;
-//  * key tiles of 32 keys; a lane owns one 16-byte pair chunk of every 8th
-//    key of the split, so its RoPE angle advances by a constant 8*theta_r per
-//    tile round (rotation recurrence, re-anchored exactly every 64 rounds);
+//    of S^T = K' Q'^T (v_mfma_f32_16x16x32_bf16) are the query heads that read
+//    this kv head (up to 16), so every key is loaded once for all of them;
+//  * all query heads of a decode step sit at one position, so the window of
+//    a cell depends on the key alone: the staging lane of a key zeroes the
+//    pairs of that key beyond their window (and skips loading pair chunks
+//    that are entirely beyond it), so the window is exact per key with no
+//    extra MFMA work; whole k-steps pruned for a tile are skipped;
+//  * key tiles of 32 keys; a lane owns one 8-pair chunk of every 8th key
+//    (16th for d = 64), so its RoPE angle advances by a constant per round
+//    (rotation recurrence, re-anchored exactly every 64 rounds);
 //  * the next tile's K chunks and V rows are loaded into registers while the
-//    current tile is computed from LDS;
-//  * partial (max, sum, unnormalised output) per split go to the caller's
-//    workspace; the combine kernel merges them.
+//    current tile is computed from LDS; V stays row-major in LDS and is read
+//    into the PV operand with the transposing LDS read;
+//  * about 180 VGPRs and 20 KB of LDS per wave: 8 waves per CU, each with a
+//    16 KB tile in flight.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,32 +31,55 @@ namespace atw {
 namespace {
 
 constexpr int kTK = 32;              // keys per tile
-constexpr int kRounds = kTK / 8;     // K staging rounds per tile (8 keys each)
 constexpr int kReanchorRounds = 64;
 constexpr float kRescaleLog2 = 8.0f;
 
-__device__ __forceinline__ int swap_bits23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8 bytes addressed by lanes i/4, i/4+4, i/4+8, i/4+12 (in that order).
+__device__ __forceinline__ v4i16 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<void*>(p));
 }
-__device__ __forceinline__ constexpr int acc_row(int v) { return 8 * (v >> 2) + (v & 3); }
 
 template <int D>
-struct DSmem {
-  __bf16 k[kTK][D + 8];              // rotated keys, pairs interleaved
-  __bf16 v[D][kTK + 8];              // V^T, keys in S^T register order
-  float2 step[D / 2];                // cos/sin of 8*theta_r
+struct DCfg {
+  static constexpr int H = D / 2;
+  static constexpr int NCH = H / 8;                 // 8-pair chunks per key
+  static constexpr int KPR = 64 / NCH;              // keys staged per round (8 or 16)
+  static constexpr int ROUNDS = kTK / KPR;          // staging rounds per tile
+  static constexpr int KROW = D + 8;                // K' row (elements), pairs interleaved
+  // V rows padded to a stride of 24 or 56 dwords mod 64: the transposing reads
+  // of two 16-lane groups (8 consecutive rows) then use disjoint banks
+  static constexpr int VROW = D == 128 ? 176 : 112;
+  static constexpr int NVT = kTK * D * 2 / 16 / 64; // 16-byte V chunks per lane per tile
+  static constexpr int NKS = D / 32;                // QK^T k-steps (16 pairs each)
+  static constexpr int ND = D / 16;                 // 16-wide head-dim blocks
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
-  constexpr int H = D / 2, NKS = D / 16, ND = D / 32;
-  constexpr int NVT = (kTK / 2) * (D / 8) / 64;    // V staging tasks per lane
+struct DSmem {
+  __bf16 k[kTK][DCfg<D>::KROW];
+  __bf16 v[kTK][DCfg<D>::VROW];
+};
+
+// BANDED: K cache stored as [batch, h_kv, h/8 bands, L, 16] (band c holds, per
+// key, dims [8c, 8c+8) then [h+8c, h+8c+8)); ks[2] is the band stride and
+// the token stride is 16.  A 128-byte line then holds one band of 4 keys,
+// so a band the window prunes for those keys is not fetched at all.
+// Otherwise K is [batch, h_kv, L, d] with ks[2] the token stride.
+template <int D, bool BANDED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(const DecodeParams p) {
+  using C = DCfg<D>;
+  constexpr int H = C::H;
   __shared__ DSmem<D> sm;
 
-  const int lane = threadIdx.x, sh = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x, l16 = lane & 15, grp4 = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int kv_len = p.kv_len[b];
-  const int64_t qpos = p.q_pos[b];
+  const int qpos = p.q_pos[b];
   const bool causal = p.causal != 0;
   const int chunk = (kv_len + p.splits - 1) / p.splits;
   const int k_begin = min(split * chunk, kv_len), k_end = min(k_begin + chunk, kv_len);
@@ -61,21 +90,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const __bf16* kbase = (const __bf16*)p.k + b * p.ks[0] + kvh * p.ks[1];
   const __bf16* vbase = (const __bf16*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
-  if (lane < H) {
-    float s, c;
-    rope_sincos(8, p.win.phi[lane], &s, &c);
-    sm.step[lane] = make_float2(c, s);
-  }
-
-  // query operand: column l32 = the l32-th query head of this kv head
-  bf16x8 qop[NKS];
+  // query operand (B of 16x16x32): column l16 = the l16-th query head of this
+  // kv head, contraction slots 8*grp4.. of k-step ks = pairs 16ks + 4grp4 + 0..3
+  bf16x8 qop[C::NKS];
   {
-    const bool valid = l32 < G;
-    const int qh = valid ? p.qh_of_kv[g0 + l32] : 0;
+    const bool valid = l16 < G;
+    const int qh = valid ? p.qh_of_kv[g0 + l16] : 0;
     const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + qh * p.qs[1];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int r0 = 8 * ks + 4 * sh;
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const int r0 = 16 * ks + 4 * grp4;
       u32x4 packed = u32x4{0, 0, 0, 0};
       if (valid) {
         const u32x2 a = *reinterpret_cast<const u32x2*>(qrow + r0);
@@ -93,243 +117,196 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     }
   }
 
-  f32x16 oacc[ND];
+  f32x4 oacc[C::ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < C::ND; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // K staging: lane = (key offset kj in 0..7, pair chunk kc in 0..7 of H/8)
-  constexpr int NCH = H / 8;
-  const int kj = lane / NCH;                  // D=128: 0..7; D=64: 0..15
-  const int kc = lane % NCH;
-  constexpr int KEYS_PER_ROUND = 64 / NCH;    // 8 (D=128) or 16 (D=64)
-  constexpr int ROUNDS = kTK / KEYS_PER_ROUND;
-  float rc[8], rs[8];
-  u32x4 kreg[ROUNDS][2];
-  u32x4 vreg[NVT][2];
+  // K staging: lane = (key offset kj, pair chunk kc); its keys are kj, kj+KPR, ...
+  // (banded: consecutive lanes take consecutive keys of one band)
+  const int kj = BANDED ? lane % C::KPR : lane / C::NCH;
+  const int kc = BANDED ? lane / C::KPR : lane % C::NCH;
+  // RoPE step of one round (KPR keys) for the lane's 8 pairs
+  float st_c[8], st_s[8], rc[8], rs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rope_sincos(C::KPR, p.win.phi[kc * 8 + e], &st_s[e], &st_c[e]);
+  // windows of the lane's 8 pairs: pair kc*8+e is dropped for a key iff dist > W
+  int wch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wch[e] = p.win.w[kc * 8 + e];
 
+  u32x4 kreg[C::ROUNDS][2];
+  u32x4 vreg[C::NVT];
   const int n_tiles = (k_end - k_begin + kTK - 1) / kTK;
 
-  auto tile_lo = [&](int t) -> int {     // first pair needed by any key of tile t
-    const int64_t m_lo = k_begin + (int64_t)t * kTK;
-    const int64_t m_hi = min(m_lo + kTK - 1, (int64_t)k_end - 1);
-    int64_t dmin = 0, dmax = 0;
-    if (!tile_distance_range(qpos, qpos, m_lo, m_hi, causal, &dmin, &dmax)) return H;
-    return wave_pairs_below(w_lane, dmin) & ~7;
+  auto key_dist = [&](int m) -> int {
+    const int d = qpos - m;
+    return (causal || d >= 0) ? d : -d;
   };
 
-  auto load_tile = [&](int t, int rlo) {
-    const int64_t m0 = k_begin + (int64_t)t * kTK;
+  auto load_tile = [&](int t) {
+    const int m0 = k_begin + t * kTK;
 #pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-      const int64_t m = m0 + KEYS_PER_ROUND * i + kj;
-      if ((kc + 1) * 8 > rlo && m < k_end) {
-        const __bf16* src = kbase + m * p.ks[2] + kc * 8;
-        kreg[i][0] = *reinterpret_cast<const u32x4*>(src);
-        kreg[i][1] = *reinterpret_cast<const u32x4*>(src + H);
+    for (int i = 0; i < C::ROUNDS; ++i) {
+      const int m = m0 + C::KPR * i + kj;
+      // the chunk is needed iff its last (longest-window) pair is kept at this key
+      if (m < k_end && key_dist(m) <= wch[7]) {
+        if constexpr (BANDED) {
+          const __bf16* src = kbase + (int64_t)kc * p.ks[2] + (int64_t)m * 16;
+          kreg[i][0] = *reinterpret_cast<const u32x4*>(src);
+          kreg[i][1] = *reinterpret_cast<const u32x4*>(src + 8);
+        } else {
+          const __bf16* src = kbase + (int64_t)m * p.ks[2] + kc * 8;
+          kreg[i][0] = *reinterpret_cast<const u32x4*>(src);
+          kreg[i][1] = *reinterpret_cast<const u32x4*>(src + H);
+        }
       } else {
         kreg[i][0] = u32x4{0, 0, 0, 0};
         kreg[i][1] = u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
-    for (int i = 0; i < NVT; ++i) {
+    for (int i = 0; i < C::NVT; ++i) {
       const int task = lane + 64 * i;
-      const int pr = task / (D / 8), dc = task % (D / 8);
-      const int64_t m = m0 + 2 * pr;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        if (m + e < k_end)
-          vreg[i][e] = *reinterpret_cast<const u32x4*>(vbase + (m + e) * p.vs[2] + dc * 8);
-        else
-          vreg[i][e] = u32x4{0, 0, 0, 0};
-      }
+      const int key = task / (D / 8), ch = task % (D / 8);
+      const int m = m0 + key;
+      if (m < k_end)
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)m * p.vs[2] + ch * 8);
+      else
+        vreg[i] = u32x4{0, 0, 0, 0};
     }
   };
 
-  int round_ix = 0;   // K staging rounds done so far (drives the recurrence)
-  auto store_tile = [&](int t, int rlo) {
-    const int64_t m0 = k_begin + (int64_t)t * kTK;
+  int round_ix = 0;   // staging rounds done so far (drives the recurrence)
+  auto store_tile = [&](int t) {
+    const int m0 = k_begin + t * kTK;
 #pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-      const int64_t m = m0 + KEYS_PER_ROUND * i + kj;
+    for (int i = 0; i < C::ROUNDS; ++i) {
+      const int m = m0 + C::KPR * i + kj;
       if (round_ix % kReanchorRounds == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) rope_sincos(m, p.win.phi[kc * 8 + e], &rs[e], &rc[e]);
       }
-      if ((kc + 1) * 8 > rlo) {
-        u32x4 o0, o1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
-          const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-          const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-          const uint32_t pk = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
-          if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
-        }
-        __bf16* dst = &sm.k[KEYS_PER_ROUND * i + kj][16 * kc];
-        reinterpret_cast<u32x4*>(dst)[0] = o0;
-        reinterpret_cast<u32x4*>(dst)[1] = o1;
-      }
-      // advance by KEYS_PER_ROUND keys: step table holds 8*theta; D=64 needs 16*theta
+      const int dist = key_dist(m);
+      u32x4 o0, o1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float2 st = sm.step[kc * 8 + e];
-        if (KEYS_PER_ROUND == 16) st = make_float2(st.x * st.x - st.y * st.y, 2.f * st.x * st.y);
+        const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
+        const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
+        const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+        uint32_t pk = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
+        pk = dist > wch[e] ? 0u : pk;             // pair beyond its window at this key
+        if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
+      }
+      __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
+      reinterpret_cast<u32x4*>(dst)[0] = o0;
+      reinterpret_cast<u32x4*>(dst)[1] = o1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         const float c = rc[e], s = rs[e];
-        rc[e] = c * st.x - s * st.y;
-        rs[e] = s * st.x + c * st.y;
+        rc[e] = c * st_c[e] - s * st_s[e];
+        rs[e] = s * st_c[e] + c * st_s[e];
       }
       ++round_ix;
     }
 #pragma unroll
-    for (int i = 0; i < NVT; ++i) {
+    for (int i = 0; i < C::NVT; ++i) {
       const int task = lane + 64 * i;
-      const int pr = task / (D / 8), dc = task % (D / 8);
-      const int pos = swap_bits23(2 * pr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vreg[i][0][e >> 1], w1 = vreg[i][1][e >> 1];
-        const uint32_t pk = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                    : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        const int row = dc * 8 + e;
-        const int unit = (pos >> 3) ^ ((row >> 2) & 3);
-        *reinterpret_cast<uint32_t*>(&sm.v[row][unit * 8 + (pos & 7)]) = pk;
-      }
+      const int key = task / (D / 8), ch = task % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.v[key][ch * 8]) = vreg[i];
     }
   };
 
-  __syncthreads();   // step table
-  int rlo = n_tiles > 0 ? tile_lo(0) : H;
-  if (n_tiles > 0) load_tile(0, rlo);
+  if (n_tiles > 0) load_tile(0);
 
   for (int t = 0; t < n_tiles; ++t) {
-    store_tile(t, rlo);
+    store_tile(t);
     __syncthreads();
-    const int rlo_next = (t + 1 < n_tiles) ? tile_lo(t + 1) : H;
-    if (t + 1 < n_tiles) load_tile(t + 1, rlo_next);
+    if (t + 1 < n_tiles) load_tile(t + 1);
 
-    const int64_t m_lo = k_begin + (int64_t)t * kTK;
-    const int64_t m_hi = min(m_lo + kTK - 1, (int64_t)k_end - 1);
+    const int m_lo = k_begin + t * kTK;
+    const int m_hi = min(m_lo + kTK - 1, k_end - 1);
     int64_t dmin = 0, dmax = 0;
-    if (tile_distance_range(qpos, qpos, m_lo, m_hi, causal, &dmin, &dmax)) {
-      const int r_any = wave_pairs_below(w_lane, dmin);
-      const int r_full = wave_pairs_below(w_lane, dmax);
-      f32x16 sacc = f32x16{};
-      const int64_t kbl = m_lo + 4 * sh;
-      const __bf16* krow = &sm.k[l32][0];
+    tile_distance_range(qpos, qpos, m_lo, m_hi, causal, &dmin, &dmax);
+    const int r_any = wave_pairs_below(w_lane, dmin);   // pairs below: zero for every key
 
-      auto drop_cells = [&](int pp) {
-        int thr_lo, thr_hi;
-        drop_bounds((int)qpos, p.win.w[pp], (int)kbl, causal, kTK, &thr_lo, &thr_hi);
+    // S^T = K' Q'^T over the k-steps that hold some kept pair
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int ko = acc_row(v);
-          if (ko < thr_lo || ko > thr_hi) sacc[v] = 0.f;
-        }
-      };
-
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      if (16 * ks + 16 <= r_any) continue;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int p0 = 8 * ks;
-        if (p0 + 8 <= r_any) continue;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 2 * (p0 + 4 * sh));
-        const u32x4 qw = __builtin_bit_cast(u32x4, qop[ks]);
-        const int plo = max(p0, r_any), phi_ = min(p0 + 8, r_full);
-        for (int pp = plo; pp < phi_; ++pp) {
-          const int u = pp - p0;
-          u32x4 bw = u32x4{0, 0, 0, 0};
-          if (sh == (u >> 2)) {
-            const int d = u & 3;
-            bw[0] = d == 0 ? qw[0] : 0u;
-            bw[1] = d == 1 ? qw[1] : 0u;
-            bw[2] = d == 2 ? qw[2] : 0u;
-            bw[3] = d == 3 ? qw[3] : 0u;
-          }
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bw), sacc, 0, 0, 0);
-          drop_cells(pp);
-        }
-        if (p0 + 8 > r_full) {
-          u32x4 bw = qw;
-          if (r_full > p0) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              if (p0 + 4 * sh + d < r_full) bw[d] = 0u;
-          }
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bw), sacc, 0, 0, 0);
-        }
+      for (int blk = 0; blk < 2; ++blk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
+        sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[blk], 0, 0, 0);
       }
-
-      // keys past the end of the split / not visible
-      if (m_lo + kTK > k_end || (causal && m_lo + kTK - 1 > qpos)) {
-        int thc, thr;
-        hide_bounds((int)qpos, (int)kbl, k_end, causal, kTK, &thc, &thr);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int ko = acc_row(v);
-          if (ko > thc || ko >= thr) sacc[v] = -INFINITY;
-        }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
-      if (__any(grow)) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * p.scale_log2);
-#pragma unroll
-        for (int i = 0; i < ND; ++i) oacc[i] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
-      float lsum = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        sacc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -mb));
-
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4 pw;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = pack_bf16(sacc[8 * g + 2 * i], sacc[8 * g + 2 * i + 1]);
-          lsum = sum_bf16x2(pw[i], lsum);     // normalizer of the rounded weights
-        }
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int bd = 0; bd < ND; ++bd) {
-          const int row = 32 * bd + l32;
-          const int unit = (2 * g + sh) ^ ((row >> 2) & 3);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.v[row][unit * 8]);
-          oacc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop, oacc[bd], 0, 0, 0);
-        }
-      }
-      l_run += lsum;
     }
-    rlo = rlo_next;
+
+    // keys past the end of the split
+    if (m_lo + kTK > k_end) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (m_lo + 16 * blk + 4 * grp4 + v >= k_end) sacc[blk][v] = -INFINITY;
+    }
+
+    // online softmax per query-head column (lanes l16, l16+16, l16+32, l16+48)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sacc[blk][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
+    if (__any(grow)) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * p.scale_log2);
+#pragma unroll
+      for (int i = 0; i < C::ND; ++i) oacc[i] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
+    // P^T operand: slots 8*grp4 + e = keys 4grp4 + e (e < 4) and 16 + 4grp4 + e - 4
+    u32x4 pw;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i >> 1][2 * (i & 1)], p.scale_log2, -mb));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i >> 1][2 * (i & 1) + 1], p.scale_log2, -mb));
+      pw[i] = pack_bf16(e0, e1);
+      lsum = sum_bf16x2(pw[i], lsum);      // normalizer of the rounded weights
+    }
+    l_run += lsum;
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+
+    // O^T += V^T P^T: transposing reads give lane l four keys of dim 16bd + l16
+#pragma unroll
+    for (int bd = 0; bd < C::ND; ++bd) {
+      const __bf16* base = &sm.v[4 * grp4 + ((lane & 15) >> 2)][16 * bd + 4 * (lane & 3)];
+      const v4i16 lo = lds_read_tr16(base);
+      const v4i16 hi = lds_read_tr16(base + 16 * C::VROW);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      oacc[bd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, oacc[bd], 0, 0, 0);
+    }
     __syncthreads();   // LDS reads done before the next store
   }
 
   // partial result of this split: [m (raw score units), l, -, -, o[D]] per query head
-  const float l_tot = half_swap_sum(l_run);
-  if (l32 < G) {
-    const int qh = p.qh_of_kv[g0 + l32];
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot = half_swap_sum(l_tot);
+  if (l16 < G) {
+    const int qh = p.qh_of_kv[g0 + l16];
     float* w = p.ws + (((int64_t)b * p.h_q + qh) * p.splits + split) * (D + 4);
-    if (sh == 0) {
+    if (grp4 == 0) {
       w[0] = m_run;
       w[1] = l_tot;
     }
 #pragma unroll
-    for (int bd = 0; bd < ND; ++bd)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int d0 = 32 * bd + 8 * v4 + 4 * sh;
-        *reinterpret_cast<f32x4*>(w + 4 + d0) =
-            f32x4{oacc[bd][4 * v4], oacc[bd][4 * v4 + 1], oacc[bd][4 * v4 + 2], oacc[bd][4 * v4 + 3]};
-      }
+    for (int bd = 0; bd < C::ND; ++bd)
+      *reinterpret_cast<f32x4*>(w + 4 + 16 * bd + 4 * grp4) = oacc[bd];
   }
 }
 
@@ -353,20 +330,52 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   o[d] = (__bf16)(acc / l);
 }
 
+// Row-layout K cache -> pair-banded K cache, for tokens [t0, t0 + n) of every
+// (batch, kv head): one thread copies the two 16-byte halves of one band of
+// one key.
+template <int D>
+__global__ __launch_bounds__(256) void kcache_band_kernel(const BandParams p) {
+  constexpr int NB = D / 16;                        // bands (8 pairs each)
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.n * NB) return;
+  const int64_t m = p.t0 + idx / NB;
+  const int c = (int)(idx % NB);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const __bf16* src = (const __bf16*)p.rows + b * p.rs[0] + h * p.rs[1] + m * p.rs[2] + 8 * c;
+  __bf16* dst = (__bf16*)p.bands + b * p.bs[0] + h * p.bs[1] + c * p.bs[2] + m * 16;
+  reinterpret_cast<u32x4*>(dst)[0] = *reinterpret_cast<const u32x4*>(src);
+  reinterpret_cast<u32x4*>(dst)[1] = *reinterpret_cast<const u32x4*>(src + D / 2);
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipStream_t stream) {
   dim3 grid((unsigned)p.splits, (unsigned)p.h_kv, (unsigned)p.batch);
   dim3 cgrid((unsigned)p.h_q, (unsigned)p.batch);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(64), 0, stream, p);
+    if (banded) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(64), 0, stream, p);
     hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(128), 0, stream, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(64), 0, stream, p);
+    if (banded) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(64), 0, stream, p);
     hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(64), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kcache_band(const BandParams& p, int head_dim, hipStream_t stream) {
+  const int64_t work = p.n * (head_dim / 16);
+  if (work <= 0) return hipSuccess;
+  dim3 grid((unsigned)((work + 255) / 256), (unsigned)p.h_kv, (unsigned)p.batch);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(kcache_band_kernel<128>, grid, dim3(256), 0, stream, p);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(kcache_band_kernel<64>, grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

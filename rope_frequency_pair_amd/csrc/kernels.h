@@ -50,6 +50,14 @@ struct DecodeParams {
   WindowArgs win;
 };
 
+struct BandParams {
+  const void* rows;
+  void* bands;
+  int64_t rs[3], bs[3];                  // (batch, head, token) / (batch, head, band) strides
+  int64_t t0, n;                         // tokens [t0, t0 + n)
+  int32_t batch, h_kv;
+};
+
 struct PlanParams {
   int32_t* plan;
   int64_t* pruned;
@@ -60,7 +68,8 @@ struct PlanParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipStream_t stream);
+hipError_t launch_kcache_band(const BandParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 
 }  // namespace atw

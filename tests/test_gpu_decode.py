@@ -91,3 +91,89 @@ def test_decode_workload_512k_sampled():
             err = max_err(to_np(out[b:b + 1, heads]), ref)
             say(f"  window_on={window_on} max abs err {err:.3e}")
             assert err <= BF16_TOL
+
+
+def _band_ref(kc):
+    """Pair-banded copy of a row cache by tensor indexing: band c of key m is
+    dims [8c, 8c+8) then [h+8c, h+8c+8)."""
+    B, H, L, D = kc.shape
+    h = D // 2
+    lo = kc[..., :h].reshape(B, H, L, D // 16, 8)
+    hi = kc[..., h:].reshape(B, H, L, D // 16, 8)
+    return torch.cat([lo, hi], dim=-1).permute(0, 1, 3, 2, 4).contiguous()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kcache_band_exact(d):
+    say(f"kcache band d={d}")
+    _, kc, _ = synth.decode_inputs(2, 4, 3, 1000, d, torch.bfloat16, 25, device="cuda")
+    bands = atw.kcache_band(kc)
+    sync()
+    assert torch.equal(bands, _band_ref(kc))
+    # append in two steps into a strided (padded) buffer: [0, 700) then [700, 1000)
+    buf = torch.zeros((2, 3, d // 16, 1024, 16), dtype=torch.bfloat16, device="cuda")
+    atw.kcache_band(kc, buf, t0=0, n_tokens=700)
+    atw.kcache_band(kc, buf, t0=700, n_tokens=300)
+    sync()
+    assert torch.equal(buf[:, :, :, :1000], _band_ref(kc))
+    assert not buf[:, :, :, 1000:].any()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 7, 64])
+def test_decode_banded_ragged_batch(d, splits):
+    """Banded cache: parity with the oracle and bit-identity with the row layout."""
+    say(f"decode banded ragged d={d} splits={splits}")
+    q, kc, vc = synth.decode_inputs(3, 8, 2, 1100, d, torch.bfloat16, 21, device="cuda")
+    kv_len = [1100, 777, 33]
+    q_pos = [1099, 776 + 50, 32]
+    rows = _check(q, kc, vc, kv_len, q_pos, 1e4, 0.5, splits)
+    bands = atw.kcache_band(kc)
+    got = atw.decode_banded(q, bands, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.5,
+                            num_splits=splits)
+    sync()
+    assert torch.equal(got, rows)
+
+
+def test_decode_banded_non_causal_window_off_head_map():
+    say("decode banded non-causal / window off / head map")
+    q, kc, vc = synth.decode_inputs(1, 6, 3, 500, 128, torch.bfloat16, 23, device="cuda")
+    bands = atw.kcache_band(kc)
+    hm = [2, 2, 0, 1, 0, 1]
+    for causal, window_on in ((False, True), (True, False)):
+        qp = [200] if not causal else [499]
+        rows = atw.decode(q, kc, vc, [500], qp, rope_base=1e4, k_turns=0.5, causal=causal,
+                          window_on=window_on, num_splits=5, kv_head_of_q=hm)
+        got = atw.decode_banded(q, bands, vc, [500], qp, rope_base=1e4, k_turns=0.5, causal=causal,
+                                window_on=window_on, num_splits=5, kv_head_of_q=hm)
+        sync()
+        assert torch.equal(got, rows)
+    _check(q, kc, vc, [500], [200], 1e4, 0.5, 5, causal=False, kv_head_of_q=hm)
+
+
+def test_decode_banded_workload_512k_sampled():
+    """The 512K decode workload over a banded cache equals the row-layout
+    result bit for bit; one (sequence, kv head) is checked against the oracle."""
+    w = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+    say("decode banded 512k: generating inputs")
+    q, kc, vc = synth.workload_decode_inputs(w)
+    L = w.n
+    G = w.h_q // w.h_kv
+    b, kvh = 5, 1
+    heads = list(range(kvh * G, (kvh + 1) * G))
+    k_rows = to_np(kc[b:b + 1, kvh:kvh + 1])
+    say("decode banded 512k: running")
+    rows = atw.decode(q, kc, vc, [L] * 8, [L] * 8, rope_base=w.rope_base, k_turns=w.k_turns,
+                      num_splits=w.splits)
+    bands = atw.kcache_band(kc)
+    del kc
+    got = atw.decode_banded(q, bands, vc, [L] * 8, [L] * 8, rope_base=w.rope_base,
+                            k_turns=w.k_turns, num_splits=w.splits)
+    sync()
+    assert torch.equal(got, rows)
+    say(f"decode banded 512k: oracle b={b} kv={kvh}")
+    ref = oracle.decode(to_np(q[b:b + 1, heads]), k_rows, to_np(vc[b:b + 1, kvh:kvh + 1]), [L], [L],
+                        w.rope_base, w.k_turns, kv_head_of_q=[0] * G)
+    err = max_err(to_np(got[b:b + 1, heads]), ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= BF16_TOL

@@ -162,3 +162,23 @@ def test_decode_invalid_arguments(lib):
     assert dec(kv=binding._arr64([0])) == atw.binding.ATW_EINVAL
     assert dec(splits=0) == atw.binding.ATW_EINVAL
     assert dec(dtype=0) == atw.binding.ATW_EUNSUPPORTED
+    # the banded entry point validates the same way
+    assert lib.atw_decode_banded(fake, fake, fake, fake, 1, 1, kv, qp, 4, 2, None, 128, s2, s3, s3,
+                                 s2, 1e4, 4.0, 1, 1, 0.0, 8, fake, need - 1,
+                                 None) == atw.binding.ATW_EWORKSPACE
+
+
+def test_kcache_band_invalid_arguments(lib):
+    s3 = binding._arr64([0, 0, 0])
+    fake = ctypes.c_void_p(16)
+
+    def band(d=128, dtype=1, t0=0, n=10, rows=fake, strides=s3):
+        return lib.atw_kcache_band(rows, fake, dtype, 1, 2, d, t0, n, strides, s3, None)
+
+    assert band(d=96) == atw.binding.ATW_EUNSUPPORTED
+    assert band(dtype=0) == atw.binding.ATW_EUNSUPPORTED
+    assert band(t0=-1) == atw.binding.ATW_EINVAL
+    assert band(t0=1 << 30) == atw.binding.ATW_EINVAL
+    assert band(rows=None) == atw.binding.ATW_EINVAL
+    assert band(strides=binding._arr64([0, 0, 3])) == atw.binding.ATW_EUNSUPPORTED
+    assert band(n=0, rows=None) == atw.binding.ATW_OK        # nothing to copy, nothing launched
