@@ -109,8 +109,9 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
  *   kv_len  host int64 [batch]: keys 0..kv_len[b]-1 of sequence b are valid (>= 1)
  *   q_pos   host int64 [batch]: position of sequence b's query; causal
  *           requires q_pos[b] >= kv_len[b] - 1 (all cached keys visible).
- *   num_splits: key-axis splits per (sequence, kv head), 1..1024; each split
- *           covers ceil(kv_len/num_splits) keys.
+ *   num_splits: key-axis splits per (sequence, kv head), 1..1024; the
+ *           splits cover consecutive key ranges of about kv_len/num_splits
+ *           keys (boundaries at multiples of 4 keys).
  *   workspace: device buffer of at least atw_decode_workspace_bytes(...)
  *           bytes for the per-split partial results (max, sum, unnormalised
  *           output); contents on entry are ignored.
@@ -142,9 +143,11 @@ size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, 
  *            of (batch, head, band); the token stride is 16 elements.
  *
  * A line then holds one band of 4 consecutive keys and is fetched only when
- * the band is inside the window for one of them.  Every other argument, the
- * result and the limits are those of atw_decode (bit-identical output for the
- * same cache contents).
+ * the band is inside the window for one of them.  The splits are sized for
+ * equal bytes rather than equal keys (a split far from the query needs fewer
+ * bands per key and covers more keys).  Every other argument, the result and
+ * the limits are those of atw_decode (same output up to fp32 rounding of the
+ * split merge; bit-identical when the window is off).
  */
 int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, void* o,
                       int32_t dtype, int64_t batch, const int64_t* kv_len, const int64_t* q_pos,

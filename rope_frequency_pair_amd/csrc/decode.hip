@@ -59,6 +59,45 @@ struct DCfg {
   static constexpr int ND = D / 16;                 // 16-wide head-dim blocks
 };
 
+// Key range of one split.  The splits of a sequence carry equal byte cost:
+// a key costs its V row plus the K bands it needs (banded cache: band c is
+// fetched for the key iff its longest-window pair, 8c+7, is kept at the key's
+// distance; row cache: every line of the row is fetched), in units of 32
+// bytes, so with the window on and a banded cache the far splits, which need
+// fewer bands, cover more keys.  Otherwise every key costs the same and the
+// splits are equal.  Boundaries are multiples of 4 keys (one 128-byte line of
+// a band) except the sequence end.
+template <int D, bool BANDED>
+__device__ void split_range(int kv_len, int qpos, bool causal, int splits, int split,
+                            const int32_t* w, int* k_begin, int* k_end) {
+  constexpr int NB = D / 16;
+  auto cost_below = [&](int x) -> int64_t {     // cost of keys [0, x)
+    int64_t c = (int64_t)(2 * D * 2 / 32) * x;  // V row: 2*D bytes
+    if (!BANDED) return c + (int64_t)NB * x;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t wb = w[8 * b + 7];
+      const int64_t lo = max((int64_t)0, (int64_t)qpos - wb);
+      const int64_t hi = causal ? (int64_t)x : min((int64_t)x, (int64_t)qpos + wb + 1);
+      c += max((int64_t)0, hi - lo);
+    }
+    return c;
+  };
+  const int64_t total = cost_below(kv_len);
+  auto bound = [&](int s) -> int {
+    if (s >= splits) return kv_len;
+    const int64_t target = total * s;
+    int lo = 0, hi = kv_len;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cost_below(mid) * splits >= target) hi = mid; else lo = mid + 1;
+    }
+    return lo & ~3;
+  };
+  *k_begin = bound(split);
+  *k_end = bound(split + 1);
+}
+
 template <int D>
 struct DSmem {
   __bf16 k[kTK][DCfg<D>::KROW];
@@ -81,8 +120,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const int kv_len = p.kv_len[b];
   const int qpos = p.q_pos[b];
   const bool causal = p.causal != 0;
-  const int chunk = (kv_len + p.splits - 1) / p.splits;
-  const int k_begin = min(split * chunk, kv_len), k_end = min(k_begin + chunk, kv_len);
+  int k_begin, k_end;
+  split_range<D, BANDED>(kv_len, qpos, causal, p.splits, split, p.win.w, &k_begin, &k_end);
 
   const int g0 = p.kv_first[kvh], G = p.kv_first[kvh + 1] - g0;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;

@@ -122,15 +122,25 @@ def test_kcache_band_exact(d):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("splits", [1, 7, 64])
 def test_decode_banded_ragged_batch(d, splits):
-    """Banded cache: parity with the oracle and bit-identity with the row layout."""
+    """Banded cache: parity with the oracle (its splits are sized by bytes, so
+    they differ from the row layout's); bit-identity with the row layout when
+    the window is off (equal splits on both)."""
     say(f"decode banded ragged d={d} splits={splits}")
     q, kc, vc = synth.decode_inputs(3, 8, 2, 1100, d, torch.bfloat16, 21, device="cuda")
     kv_len = [1100, 777, 33]
     q_pos = [1099, 776 + 50, 32]
-    rows = _check(q, kc, vc, kv_len, q_pos, 1e4, 0.5, splits)
     bands = atw.kcache_band(kc)
     got = atw.decode_banded(q, bands, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.5,
                             num_splits=splits)
+    sync()
+    ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.5)
+    err = max_err(to_np(got), ref)
+    say(f"  banded max abs err {err:.3e}")
+    assert err <= BF16_TOL
+    rows = atw.decode(q, kc, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.5, window_on=False,
+                      num_splits=splits)
+    got = atw.decode_banded(q, bands, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.5,
+                            window_on=False, num_splits=splits)
     sync()
     assert torch.equal(got, rows)
 
@@ -140,20 +150,20 @@ def test_decode_banded_non_causal_window_off_head_map():
     q, kc, vc = synth.decode_inputs(1, 6, 3, 500, 128, torch.bfloat16, 23, device="cuda")
     bands = atw.kcache_band(kc)
     hm = [2, 2, 0, 1, 0, 1]
-    for causal, window_on in ((False, True), (True, False)):
-        qp = [200] if not causal else [499]
-        rows = atw.decode(q, kc, vc, [500], qp, rope_base=1e4, k_turns=0.5, causal=causal,
-                          window_on=window_on, num_splits=5, kv_head_of_q=hm)
-        got = atw.decode_banded(q, bands, vc, [500], qp, rope_base=1e4, k_turns=0.5, causal=causal,
-                                window_on=window_on, num_splits=5, kv_head_of_q=hm)
+    for causal, window_on, qp in ((False, True, 200), (True, True, 499), (True, False, 499)):
+        got = atw.decode_banded(q, bands, vc, [500], [qp], rope_base=1e4, k_turns=0.5,
+                                causal=causal, window_on=window_on, num_splits=5, kv_head_of_q=hm)
         sync()
-        assert torch.equal(got, rows)
-    _check(q, kc, vc, [500], [200], 1e4, 0.5, 5, causal=False, kv_head_of_q=hm)
+        ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), [500], [qp], 1e4, 0.5, causal=causal,
+                            window_on=window_on, kv_head_of_q=hm)
+        err = max_err(to_np(got), ref)
+        say(f"  causal={causal} window_on={window_on} max abs err {err:.3e}")
+        assert err <= BF16_TOL
 
 
 def test_decode_banded_workload_512k_sampled():
-    """The 512K decode workload over a banded cache equals the row-layout
-    result bit for bit; one (sequence, kv head) is checked against the oracle."""
+    """The 512K decode workload over a banded cache: one (sequence, kv head)
+    against the oracle, every output against the row-layout result."""
     w = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
     say("decode banded 512k: generating inputs")
     q, kc, vc = synth.workload_decode_inputs(w)
@@ -170,7 +180,7 @@ def test_decode_banded_workload_512k_sampled():
     got = atw.decode_banded(q, bands, vc, [L] * 8, [L] * 8, rope_base=w.rope_base,
                             k_turns=w.k_turns, num_splits=w.splits)
     sync()
-    assert torch.equal(got, rows)
+    assert max_err(to_np(got), to_np(rows).astype(np.float64)) <= 2 * BF16_TOL
     say(f"decode banded 512k: oracle b={b} kv={kvh}")
     ref = oracle.decode(to_np(q[b:b + 1, heads]), k_rows, to_np(vc[b:b + 1, kvh:kvh + 1]), [L], [L],
                         w.rope_base, w.k_turns, kv_head_of_q=[0] * G)
