@@ -28,9 +28,9 @@
  *   - Element strides are given per tensor as int64 element counts; the head
  *     dimension is contiguous (stride 1).  Base pointers must be 16-byte
  *     aligned and every stride a multiple of 16 bytes / element size.
- *   - Every device pointer is allocated and owned by the caller; the library
- *     allocates no device memory and keeps no state between calls except a
- *     thread-local error string.  Inputs are never written; outputs are fully
+ *   - Every device pointer (workspaces included) is allocated and owned by
+ *     the caller; the library allocates no device memory and keeps no state
+ *     between calls except a thread-local error string.  Inputs are never written; outputs are fully
  *     written.
  *   - Calls are asynchronous on the given HIP stream (hipStream_t, passed as
  *     void*; NULL = the default stream).  Execution errors surface when the
@@ -84,8 +84,13 @@ extern "C" {
  *     passes q_pos0 = tokens already cached and n_kv = q_pos0 + n_q);
  *     0 = every key visible, window on |n - m|.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   workspace: device buffer of at least atw_prefill_workspace_bytes(...)
+ *     bytes (ATW_BF16: the keys rotated once and the values, both re-ordered
+ *     into matrix-core operand order, 64-key tiles; ATW_F32: none needed, may
+ *     be NULL).  Contents on entry are ignored; overwritten by the call.
  * Requires n_q >= 0, n_kv >= 1, q_pos0 >= 0, h_q % h_kv == 0 without a map,
- * rope_base > 1, k_turns > 0 when window_on.  n_q = 0 launches nothing.
+ * rope_base > 1, k_turns > 0 when window_on, batch <= 65535.  n_q = 0
+ * launches nothing.
  */
 int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
                 int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0,
@@ -93,7 +98,12 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
                 const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
                 const int64_t* o_strides,
                 double rope_base, double k_turns, int32_t causal, int32_t window_on,
-                double softmax_scale, void* stream);
+                double softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes atw_prefill needs: ATW_BF16: 2 * batch * h_kv *
+ * ceil(n_kv / 64) * 64 * head_dim * 2 (one copy of K and V); ATW_F32: 0. */
+size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,
+                                   int32_t head_dim);
 
 /*
  * atw_decode -- one query token per sequence against a pre-RoPE KV cache,

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     default_scale,
     load_library,
     prefill,
+    prefill_workspace_bytes,
     pruned_terms,
     version,
     window_plan,

@@ -17,7 +17,7 @@ ATW_F32, ATW_BF16 = 0, 1
 UNBOUNDED = 1 << 62
 
 EXPORTED = [
-    "atw_prefill", "atw_decode", "atw_decode_banded", "atw_kcache_band",
+    "atw_prefill", "atw_prefill_workspace_bytes", "atw_decode", "atw_decode_banded", "atw_kcache_band",
     "atw_decode_workspace_bytes", "atw_pruned_terms",
     "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
     "atw_version",
@@ -47,8 +47,11 @@ def load_library(path=LIB_PATH):
                            "(hipcc, gfx950) first; there is no fallback path")
     lib = ctypes.CDLL(path)
     lib.atw_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _pi32,
-                                _i32, _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _vp]
+                                _i32, _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _vp,
+                                ctypes.c_size_t, _vp]
     lib.atw_prefill.restype = ctypes.c_int
+    lib.atw_prefill_workspace_bytes.argtypes = [_i32, _i64, _i32, _i64, _i32]
+    lib.atw_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.atw_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _pi64, _pi64, _i32, _i32, _pi32, _i32,
                                _pi64, _pi64, _pi64, _pi64, _f64, _f64, _i32, _i32, _f64, _i32, _vp,
                                ctypes.c_size_t, _vp]
@@ -162,10 +165,16 @@ def window_plan_device(head_dim, rope_base, k_turns, window_on, n_q, n_kv, q_pos
     return plan, pruned
 
 
+def prefill_workspace_bytes(dtype_code, batch, h_kv, n_kv, head_dim):
+    return load_library().atw_prefill_workspace_bytes(dtype_code, batch, h_kv, n_kv, head_dim)
+
+
 def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=True, scale=None,
-            kv_head_of_q=None, out=None, stream=None):
+            kv_head_of_q=None, out=None, workspace=None, stream=None):
     """Windowed prefill.  q [B, Hq, Nq, d]; k, v [B, Hkv, Nkv, d] (any strides
-    with d contiguous), bf16 or fp32 CUDA tensors.  Returns out [B, Hq, Nq, d]."""
+    with d contiguous), bf16 or fp32 CUDA tensors.  Returns out [B, Hq, Nq, d].
+    workspace: device buffer of prefill_workspace_bytes(...) bytes, allocated
+    per call when None."""
     import torch
     lib = load_library()
     if out is None:
@@ -175,12 +184,17 @@ def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=Tru
             raise AtwError(ATW_EINVAL, f"{name} must be 4-D with a contiguous last dim")
     B, Hq, Nq, D = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
+    need = lib.atw_prefill_workspace_bytes(_dtype_code(q), B, Hkv, Nkv, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.atw_prefill(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
         _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
         _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), float(rope_base), float(k_turns),
-        int(causal), int(window_on), float(scale or 0.0), _stream_ptr(stream)))
+        int(causal), int(window_on), float(scale or 0.0), ws_ptr, ws_len, _stream_ptr(stream)))
     return out
 
 

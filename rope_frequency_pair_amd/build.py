@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libatw.so")
 
-SOURCES = ["atw_api.cpp", "planner.cpp", "prefill_f32.hip", "decode.hip", "plan.hip"]
+SOURCES = ["atw_api.cpp", "planner.cpp", "prefill.hip", "prefill_f32.hip", "decode.hip", "plan.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -171,7 +171,7 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
                 const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
                 const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
                 double rope_base, double k_turns, int32_t causal, int32_t window_on,
-                double softmax_scale, void* stream) {
+                double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "prefill supports head_dim 64 and 128 (got %d)", head_dim);
@@ -194,6 +194,11 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
   if (int e = check_strides("o", o_strides, 3, elem)) return e;
   const int64_t n_qblk = (n_q + atw::kPrefillBlockRows - 1) / atw::kPrefillBlockRows;
   if (n_qblk * h_q * batch >= (int64_t(1) << 31)) return fail(ATW_EUNSUPPORTED, "grid too large");
+  if (batch > 65535) return fail(ATW_EUNSUPPORTED, "batch must be <= 65535");
+  const size_t need = atw_prefill_workspace_bytes(dtype, batch, h_kv, n_kv, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATW_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(ATW_EUNSUPPORTED, "workspace must be 16-byte aligned");
 
   atw::PrefillParams p{};
   p.q = q;
@@ -225,7 +230,34 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
   }
   p.kv_first[h_kv] = (int16_t)n;
   fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
-  return hip_status(atw::launch_prefill(p, dtype, head_dim, (hipStream_t)stream), "prefill launch");
+  if (dtype == ATW_F32)
+    return hip_status(atw::launch_prefill_f32(p, head_dim, (hipStream_t)stream), "prefill launch");
+
+  atw::PackParams pk{};
+  pk.k = k;
+  pk.v = v;
+  const size_t half = need / 2;
+  pk.kp = workspace;
+  pk.vp = static_cast<char*>(workspace) + half;
+  for (int i = 0; i < 3; ++i) {
+    pk.ks[i] = k_strides[i];
+    pk.vs[i] = v_strides[i];
+  }
+  pk.n_kv = (int32_t)n_kv;
+  pk.n_kt = (int32_t)((n_kv + atw::kPrefillTileK - 1) / atw::kPrefillTileK);
+  pk.h_kv = h_kv;
+  pk.batch = (int32_t)batch;
+  pk.win = p.win;
+  p.kp = pk.kp;
+  p.vp = pk.vp;
+  p.n_kt = pk.n_kt;
+  return hip_status(atw::launch_prefill_bf16(p, pk, head_dim, (hipStream_t)stream), "prefill launch");
+}
+
+size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,
+                                   int32_t head_dim) {
+  if (dtype != ATW_BF16 || batch <= 0 || h_kv <= 0 || n_kv <= 0 || head_dim <= 0) return 0;
+  return atw::prefill_pack_bytes(batch, h_kv, n_kv, head_dim);
 }
 
 size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits) {

@@ -21,9 +21,12 @@ struct PrefillParams {
   const void* k;
   const void* v;
   void* o;
+  const void* kp;                        // bf16: packed K' / V tiles (pack_kv_kernel)
+  const void* vp;
   int64_t qs[3], ks[3], vs[3], os[3];   // element strides (batch, head, token)
   int32_t batch, n_q, n_kv, q_pos0;
   int32_t h_q, causal, n_qblk, n_kv_heads;
+  int32_t n_kt;                          // packed key tiles per (batch, kv head)
   float scale_log2;                      // softmax scale * log2(e)
   int16_t qh_of_kv[kMaxHeadsQ];          // query heads grouped by kv head (kv-major)
   int16_t kv_first[kMaxHeadsQ + 1];      // start of each kv head's group in qh_of_kv
@@ -50,6 +53,24 @@ struct DecodeParams {
   WindowArgs win;
 };
 
+// Packing of K (rotated) and V into matrix-core operand order, 64-key tiles:
+// kp/vp [batch, h_kv, n_kt, 64 * head_dim] bf16.
+struct PackParams {
+  const void* k;
+  const void* v;
+  void* kp;
+  void* vp;
+  int64_t ks[3], vs[3];
+  int32_t n_kv, n_kt, h_kv, batch;
+  WindowArgs win;
+};
+
+// Bytes of the packed K' + V tiles of a bf16 prefill.
+inline size_t prefill_pack_bytes(int64_t batch, int64_t h_kv, int64_t n_kv, int64_t head_dim) {
+  const int64_t n_kt = (n_kv + kPrefillTileK - 1) / kPrefillTileK;
+  return (size_t)(2 * batch * h_kv * n_kt * kPrefillTileK * head_dim * 2);
+}
+
 struct BandParams {
   const void* rows;
   void* bands;
@@ -67,7 +88,9 @@ struct PlanParams {
   WindowArgs win;
 };
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int head_dim,
+                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipStream_t stream);
 hipError_t launch_kcache_band(const BandParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);

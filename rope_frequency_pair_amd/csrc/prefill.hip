@@ -1,0 +1,487 @@
+// Windowed causal prefill, bf16, for gfx950 (MI355X).
+//
+// Method: "ATFlash — Per-RoPE-Wavelength Attention Windows", README, "The
+// idea" and "Porting to something else": the window is a slice of the
+// query-key contraction axis.  For a key tile, the pairs whose window is
+// shorter than the tile's smallest query-key distance are never needed, so
+// that part of the key tile is never loaded and its products are never
+// issued.  The online softmax (running max, normalizer) is the ordinary one.
+//
+// Two kernels (designed for CDNA4, not taken from the pages):
+//
+//  pack_kv_kernel -- once per call, rotates every key at its position
+//    (RoPE) and writes K' and V in the order the matrix-core operands are
+//    read: a 64-key tile is a run of 1 KB blocks, one block per (operand,
+//    wave-wide read), lane l's 16 bytes at l * 16.  The pages fuse RoPE into
+//    the attention loads; here every key tile is read by every query block
+//    of its head, so rotating it there repeats the same work hundreds of
+//    times on the vector ALUs, which bound the loop on this GPU.  One pass
+//    over K and V (a fraction of a percent of the attention time) removes it.
+//
+//  prefill_bf16_kernel -- one workgroup = 8 waves = 256 consecutive query
+//    rows of one query head; a wave owns 32 rows; key tiles of 64 keys,
+//    double-buffered in LDS:
+//  * staging is a plain copy of 1 KB blocks (wave w copies blocks w, w+8,
+//    ...); K' blocks of k-steps that the window prunes for the whole
+//    workgroup are neither loaded nor written;
+//  * workgroups are dispatched largest causal blocks first, and the ones
+//    resident on one XCD (workgroup i runs on XCD i mod 8) are consecutive
+//    blocks of one (batch, kv head), so they share K'/V tiles in its L2;
+//  * scores are computed transposed, S^T = K' Q'^T, with
+//    v_mfma_f32_32x32x16_bf16, so each lane holds 16 keys of one query
+//    column and the row max / sum are mostly in-lane; lanes l and l+32 share
+//    a query;
+//  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
+//    k-step of 16 covers 8 whole pairs, so the retained pairs [r, h) are a
+//    contiguous range of k-steps;
+//  * pairs that are in the window for some cells of a wave's tile and not for
+//    others ("partial" pairs) are added first, one pair per MFMA, and after
+//    each such pair the cells beyond its window are reset to zero; because
+//    windows grow with r, this leaves exactly the kept partial terms; the
+//    fully kept pairs are added after;
+//  * O^T += V^T P^T with P^T taken straight from the S^T registers (V is
+//    packed in the key order that register layout produces);
+//  * waves 0-3 run each tile as [QK^T, softmax, PV, staging of the next
+//    tile] and waves 4-7 as [staging, QK^T, softmax, PV], so on each SIMD
+//    the MFMA stretches of one wave meet the VALU stretches of the other;
+//    one workgroup barrier per tile;
+//  * lazy rescaling of the output when the running max grows by more than
+//    2^8 (the softmax result is unchanged, only fewer rescales).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace atw {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsW = 32;
+constexpr int kTK = kPrefillTileK;
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D>
+struct PCfg {
+  static constexpr int H = D / 2;
+  static constexpr int NKS = D / 16;      // QK^T k-steps (8 pairs each)
+  static constexpr int ND = D / 32;       // 32-wide head-dim blocks of O^T
+  static constexpr int KBLK = 2 * NKS;    // K' blocks per tile: (k-step, 32-key block)
+  static constexpr int VBLK = 4 * ND;     // V blocks per tile: (head-dim block, 16-key group)
+  static constexpr int KPW = KBLK / kWaves;
+  static constexpr int VPW = VBLK / kWaves;
+  static_assert(KPW >= 1 && VPW >= 1, "head_dim 64 or 128");
+};
+
+// Element offset of the 8 bf16 values lane `lane` reads from operand block
+// `blk` of a packed tile.
+__device__ __forceinline__ int blk_off(int blk, int lane) { return (blk * 64 + lane) * 8; }
+
+// Key offset (within a 32-key block, before + 4*s) of accumulator register v
+// in the 32x32 MFMA output layout.
+__device__ __forceinline__ constexpr int acc_row(int v) { return 8 * (v >> 2) + (v & 3); }
+
+// Key (within a 64-key tile) of slot j of lane half s in PV key group g: the
+// order in which the S^T accumulator registers hold the keys.
+__device__ __forceinline__ constexpr int pv_key(int g, int s, int j) {
+  return 32 * (g >> 1) + 16 * (g & 1) + 8 * (j >> 2) + 4 * s + (j & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
+  using C = PCfg<D>;
+  constexpr int H = C::H;
+  constexpr int ROW = D + 8;                     // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) __bf16 sk[kTK][ROW];
+  __shared__ __attribute__((aligned(16))) __bf16 sv[kTK][ROW];
+
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int m0 = tile * kTK;
+  const __bf16* kb = (const __bf16*)p.k + b * p.ks[0] + h * p.ks[1];
+  const __bf16* vb = (const __bf16*)p.v + b * p.vs[0] + h * p.vs[1];
+  const int64_t tix = ((int64_t)b * p.h_kv + h) * p.n_kt + tile;
+  __bf16* kp = (__bf16*)p.kp + tix * (kTK * D);
+  __bf16* vp = (__bf16*)p.vp + tix * (kTK * D);
+
+  // row-major copy of the tile into LDS; keys past n_kv are zero
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  for (int c = tid; c < kTK * CPR; c += 256) {
+    const int key = c / CPR, ch = c % CPR;
+    const int m = m0 + key;
+    u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
+    if (m < p.n_kv) {
+      x = *reinterpret_cast<const u32x4*>(kb + (int64_t)m * p.ks[2] + ch * 8);
+      y = *reinterpret_cast<const u32x4*>(vb + (int64_t)m * p.vs[2] + ch * 8);
+    }
+    *reinterpret_cast<u32x4*>(&sk[key][ch * 8]) = x;
+    *reinterpret_cast<u32x4*>(&sv[key][ch * 8]) = y;
+  }
+  __syncthreads();
+
+  // K' blocks: lane l of block (ks, blk) holds key 32*blk + l%32, pairs
+  // 8*ks + 4*(l/32) + u, u = 0..3, rotated, as (x_r, x_{r+h}) bf16 pairs
+  for (int it = tid; it < C::KBLK * 64; it += 256) {
+    const int blk = it >> 6, lane = it & 63;
+    const int key = 32 * (blk & 1) + (lane & 31);
+    const int r0 = 8 * (blk >> 1) + 4 * (lane >> 5);
+    const int m = m0 + key;
+    u32x4 out;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float x1 = (float)sk[key][r0 + u], x2 = (float)sk[key][H + r0 + u];
+      float s, c;
+      rope_sincos(m, p.win.phi[r0 + u], &s, &c);
+      out[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
+    }
+    *reinterpret_cast<u32x4*>(kp + blk_off(blk, lane)) = out;
+  }
+  // V blocks: lane l of block (bd, g) holds head-dim 32*bd + l%32 of keys
+  // pv_key(g, l/32, j), j = 0..7
+  for (int it = tid; it < C::VBLK * 64; it += 256) {
+    const int blk = it >> 6, lane = it & 63;
+    const int bd = blk >> 2, g = blk & 3;
+    const int dim = 32 * bd + (lane & 31), s = lane >> 5;
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      bf16x2 w;
+      w[0] = sv[pv_key(g, s, j)][dim];
+      w[1] = sv[pv_key(g, s, j + 1)][dim];
+      out[j >> 1] = __builtin_bit_cast(uint32_t, w);
+    }
+    *reinterpret_cast<u32x4*>(vp + blk_off(blk, lane)) = out;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillParams p) {
+  using C = PCfg<D>;
+  constexpr int H = C::H;
+  constexpr int TILE = kTK * D;
+  __shared__ __attribute__((aligned(16))) __bf16 lk[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lv[2][TILE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sh = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;   // 0: waves 0-3, 1: waves 4-7 (one phase later)
+
+  // ---- work item.  The list (batch, kv head, query block descending, query
+  // head) is mapped onto the XCDs (XCD x runs workgroups x, x+8, ...):
+  //  * when the (batch, kv head) groups split evenly over the 8 XCDs, XCD x
+  //    takes a contiguous eighth of the list (whole groups: its L2 serves
+  //    only its own kv heads);
+  //  * otherwise the list is dealt in rounds of 8 x 32 entries, XCD x taking
+  //    32 consecutive entries per round, which balances the causal work;
+  // the last partial round keeps the identity order.
+  int bb, hq, qb, kvh;
+  {
+    constexpr int kRound = 32;
+    const int W = p.n_qblk * p.h_q * p.batch;
+    const int idx = (int)blockIdx.x, x = idx & 7, li = idx >> 3;
+    int pos;
+    if ((p.batch * p.n_kv_heads) % 8 == 0 && W % 8 == 0) {
+      pos = x * (W >> 3) + li;
+    } else {
+      const int full = W / (8 * kRound);
+      const int round = li / kRound;
+      pos = (round < full) ? round * 8 * kRound + x * kRound + li % kRound : idx;
+    }
+    const int per_b = p.n_qblk * p.h_q;
+    bb = pos / per_b;
+    const int r = pos - bb * per_b;
+    int j = 0;
+    while ((int)p.kv_first[j + 1] * p.n_qblk <= r) ++j;
+    const int r2 = r - (int)p.kv_first[j] * p.n_qblk;
+    const int G = p.kv_first[j + 1] - p.kv_first[j];
+    qb = p.n_qblk - 1 - r2 / G;
+    hq = p.qh_of_kv[p.kv_first[j] + r2 % G];
+    kvh = j;
+  }
+
+  const __bf16* qbase = (const __bf16*)p.q + bb * p.qs[0] + hq * p.qs[1];
+  __bf16* obase = (__bf16*)p.o + bb * p.os[0] + hq * p.os[1];
+  const int64_t tix0 = ((int64_t)bb * p.n_kv_heads + kvh) * p.n_kt;
+  const __bf16* kpk = (const __bf16*)p.kp + tix0 * TILE;
+  const __bf16* vpk = (const __bf16*)p.vp + tix0 * TILE;
+
+  const bool causal = p.causal != 0;
+  const int n_kv = p.n_kv;
+  const int i0 = qb * kPrefillBlockRows;
+  const int g_last = min(i0 + kPrefillBlockRows - 1, p.n_q - 1);
+  const int w_first = i0 + wave * kRowsW;
+  const int w_last = min(w_first + kRowsW - 1, p.n_q - 1);
+  const bool wave_rows = w_first <= w_last;
+  const int n_lo = p.q_pos0 + w_first, n_hi = p.q_pos0 + w_last;
+  const int gn_lo = p.q_pos0 + i0, gn_hi = p.q_pos0 + g_last;
+  const int qrow = min(w_first + l32, p.n_q - 1);
+  const int npos = p.q_pos0 + qrow;
+  const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
+
+  // ---- query: load, rotate at its position, keep as MFMA operand (lane l:
+  // query l%32, pairs 8ks + 4(l/32) + u as (x_r, x_{r+h}) pairs)
+  const __bf16* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
+  bf16x8 qop[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    const int r0 = 8 * ks + 4 * sh;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(qrow_ptr + r0);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(qrow_ptr + H + r0);
+    u32x4 packed;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
+      const float x2 = (u & 1) ? bf16_hi(b[u >> 1]) : bf16_lo(b[u >> 1]);
+      float s, c;
+      rope_sincos(npos, p.win.phi[r0 + u], &s, &c);
+      packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
+    }
+    qop[ks] = __builtin_bit_cast(bf16x8, packed);
+  }
+
+  f32x16 oacc[C::ND];
+#pragma unroll
+  for (int b = 0; b < C::ND; ++b) oacc[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_end = causal ? min(n_kv, gn_hi + 1) : n_kv;
+  const int n_kt = (kv_end + kTK - 1) / kTK;
+
+  // ---- staging: wave w copies K' blocks w + 8i and V blocks w + 8i
+  // First k-step any cell of the workgroup needs in key tile t (wave-uniform).
+  auto stage_ks = [&](int t) -> int {
+    const int m_lo = t * kTK;
+    const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
+    int64_t dmin = 0, dmax = 0;
+    if (!tile_distance_range(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return C::NKS;
+    return wave_pairs_below(w_lane, dmin) >> 3;
+  };
+  u32x4 kreg[C::KPW], vreg[C::VPW];
+  int pend_ks = 0;   // stage_ks of the tile held in kreg / vreg
+  auto load = [&](int t) {
+    pend_ks = stage_ks(t);
+    const __bf16* ks = kpk + (int64_t)t * TILE;
+    const __bf16* vs = vpk + (int64_t)t * TILE;
+#pragma unroll
+    for (int i = 0; i < C::KPW; ++i) {
+      const int blk = wave + kWaves * i;
+      if ((blk >> 1) >= pend_ks) kreg[i] = *reinterpret_cast<const u32x4*>(ks + blk_off(blk, lane));
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i)
+      vreg[i] = *reinterpret_cast<const u32x4*>(vs + blk_off(wave + kWaves * i, lane));
+  };
+  auto write = [&](int t) {
+    __bf16* kd = &lk[t & 1][0];
+    __bf16* vd = &lv[t & 1][0];
+#pragma unroll
+    for (int i = 0; i < C::KPW; ++i) {
+      const int blk = wave + kWaves * i;
+      if ((blk >> 1) >= pend_ks) *reinterpret_cast<u32x4*>(kd + blk_off(blk, lane)) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i)
+      *reinterpret_cast<u32x4*>(vd + blk_off(wave + kWaves * i, lane)) = vreg[i];
+  };
+
+  // ---- prologue: tile 0 by everyone; waves 4-7 also load tile 1
+  load(0);
+  write(0);
+  if (grp == 1 && n_kt > 1) load(1);
+  __syncthreads();
+
+  for (int t = 0; t < n_kt; ++t) {
+    if (grp == 0) {
+      if (t + 1 < n_kt) load(t + 1);
+    } else {
+      if (t + 1 < n_kt) write(t + 1);
+      if (t + 2 < n_kt) load(t + 2);
+    }
+
+    const int m_lo = t * kTK;
+    const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
+    int64_t dmin = 0, dmax = 0;
+    if (wave_rows && tile_distance_range(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
+      const int r_any = wave_pairs_below(w_lane, dmin);
+      const int r_full = wave_pairs_below(w_lane, dmax);
+      const int kbase_lane = m_lo + 4 * sh;
+      const __bf16* kt = &lk[t & 1][0];
+      const __bf16* vt = &lv[t & 1][0];
+      f32x16 sacc[2];
+
+      // reset the cells of x beyond the window of partially windowed pair pp
+      auto drop_cells = [&](f32x16 (&x)[2], int pp) {
+        int thr_lo, thr_hi;
+        drop_bounds(npos, p.win.w[pp], kbase_lane, causal, kTK, &thr_lo, &thr_hi);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ko = 32 * blk + acc_row(v);
+            if (ko < thr_lo || ko > thr_hi) x[blk][v] = 0.f;
+          }
+      };
+      auto kop = [&](int ks, int blk) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(kt + blk_off(2 * ks + blk, lane));
+      };
+
+      // pairs kept for every cell: k-steps kk0..NKS-1, taken from the top so
+      // the first MFMA starts from a zero accumulator; the operands of the
+      // next k-step are read from LDS while the current one multiplies
+      const int kk0 = r_full >> 3;
+      if (kk0 < C::NKS) {
+        bf16x8 na0 = kop(C::NKS - 1, 0), na1 = kop(C::NKS - 1, 1);
+#pragma unroll
+        for (int ks = C::NKS - 1; ks >= 0; --ks) {
+          if (ks < kk0) break;
+          const bf16x8 a0 = na0, a1 = na1;
+          if (ks > kk0) {
+            na0 = kop(ks - 1, 0);
+            na1 = kop(ks - 1, 1);
+          }
+          u32x4 bw = __builtin_bit_cast(u32x4, qop[ks]);
+          if (ks == kk0 && (r_full & 7)) {   // pairs below r_full of this k-step are partial
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              if (8 * ks + 4 * sh + d < r_full) bw[d] = 0u;
+          }
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+          if (ks == C::NKS - 1) {
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, f32x16{}, 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, f32x16{}, 0, 0, 0);
+          } else {
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
+          }
+        }
+      } else {
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+      }
+      // partially windowed pairs [r_any, r_full): one pair per MFMA into a
+      // separate accumulator, ascending, each followed by the reset
+      if (r_any < r_full) {
+        f32x16 x[2] = {f32x16{}, f32x16{}};
+        for (int pp = r_any; pp < r_full; ++pp) {
+          const int ks = pp >> 3, uu = pp & 7;
+          const bf16x8 a0 = kop(ks, 0), a1 = kop(ks, 1);
+          uint32_t qd = 0u;
+#pragma unroll
+          for (int k2 = 0; k2 < C::NKS; ++k2) {
+            const u32x4 qw = __builtin_bit_cast(u32x4, qop[k2]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) qd = (k2 == ks && d == (uu & 3)) ? qw[d] : qd;
+          }
+          const bool mine = sh == (uu >> 2);
+          u32x4 bw;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+          x[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, x[0], 0, 0, 0);
+          x[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, x[1], 0, 0, 0);
+          drop_cells(x, pp);
+        }
+        sacc[0] += x[0];
+        sacc[1] += x[1];
+      }
+
+      // causal and ragged-tail masks (cells outside the attended set)
+      const bool need_mask = (causal && m_lo + kTK - 1 > n_lo) || (m_lo + kTK > n_kv);
+      if (need_mask) {
+        int thc, thr;
+        hide_bounds(npos, kbase_lane, n_kv, causal, kTK, &thc, &thr);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ko = 32 * blk + acc_row(v);
+            if (ko > thc || ko >= thr) sacc[blk][v] = -INFINITY;
+          }
+      }
+
+      // online softmax (base 2, scale folded into the exponent)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[blk][v]);
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * p.scale_log2);
+#pragma unroll
+        for (int b = 0; b < C::ND; ++b) oacc[b] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
+      float lsum = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // V operands of this key group first, so their LDS latency overlaps
+        // the exponentials below
+        bf16x8 va[C::ND];
+#pragma unroll
+        for (int b = 0; b < C::ND; ++b)
+          va[b] = *reinterpret_cast<const bf16x8*>(vt + blk_off(4 * b + g, lane));
+        u32x4 pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v0 = 8 * (g & 1) + 2 * i;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0], p.scale_log2, -mb));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0 + 1], p.scale_log2, -mb));
+          pw[i] = pack_bf16(e0, e1);
+          // the normalizer sums the same rounded weights the PV product uses
+          lsum = sum_bf16x2(pw[i], lsum);
+        }
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int b = 0; b < C::ND; ++b)
+          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[b], pop, oacc[b], 0, 0, 0);
+      }
+      l_run += lsum;
+    }
+
+    if (grp == 0 && t + 1 < n_kt) write(t + 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = 1.f / l_tot;
+  const int row = w_first + l32;
+  if (wave_rows && row <= w_last) {
+    __bf16* orow = obase + (int64_t)row * p.os[2];
+#pragma unroll
+    for (int b = 0; b < C::ND; ++b)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * b + 8 * v4 + 4 * sh;
+        u32x2 w;
+        w[0] = pack_bf16(oacc[b][4 * v4] * inv, oacc[b][4 * v4 + 1] * inv);
+        w[1] = pack_bf16(oacc[b][4 * v4 + 2] * inv, oacc[b][4 * v4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int head_dim,
+                               hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_qblk * p.h_q * p.batch;
+  if (blocks <= 0) return hipSuccess;
+  dim3 pgrid((unsigned)pk.n_kt, (unsigned)pk.h_kv, (unsigned)pk.batch);
+  dim3 grid((unsigned)blocks), block(kThreads);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(pack_kv_kernel<128>, pgrid, dim3(256), 0, stream, pk);
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, p);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL(pack_kv_kernel<64>, pgrid, dim3(256), 0, stream, pk);
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace atw

@@ -595,17 +595,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream) {
+hipError_t launch_prefill_f32(const PrefillParams& p, int head_dim, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_qblk * p.h_q * p.batch;
   if (blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)blocks), block(kThreads);
-  if (dtype == 1 && head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<__bf16, 128>), grid, block, 0, stream, p);
-  else if (dtype == 1 && head_dim == 64)
-    hipLaunchKernelGGL((prefill_kernel<__bf16, 64>), grid, block, 0, stream, p);
-  else if (dtype == 0 && head_dim == 128)
+  if (head_dim == 128)
     hipLaunchKernelGGL((prefill_kernel<float, 128>), grid, block, 0, stream, p);
-  else if (dtype == 0 && head_dim == 64)
+  else if (head_dim == 64)
     hipLaunchKernelGGL((prefill_kernel<float, 64>), grid, block, 0, stream, p);
   else
     return hipErrorInvalidValue;

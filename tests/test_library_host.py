@@ -129,7 +129,7 @@ def test_invalid_arguments(lib):
         a = dict(args, **kw)
         return lib.atw_prefill(fake, fake, fake, fake, a["dtype"], a["batch"], a["n_q"], a["n_kv"],
                                a["q_pos0"], a["h_q"], a["h_kv"], None, a["d"], s, s, s, s, 1e4, 4.0, 1,
-                               1, 0.0, None)
+                               1, 0.0, fake, a.get("ws", 1 << 40), None)
 
     assert pre(d=96) == atw.binding.ATW_EUNSUPPORTED
     assert pre(dtype=7) == atw.binding.ATW_EUNSUPPORTED
@@ -137,13 +137,18 @@ def test_invalid_arguments(lib):
     assert pre(n_kv=0) == atw.binding.ATW_EINVAL
     assert pre(batch=0) == atw.binding.ATW_EINVAL
     assert lib.atw_prefill(None, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, None, 128, s, s, s, s, 1e4,
-                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EINVAL
+                           4.0, 1, 1, 0.0, fake, 1 << 40, None) == atw.binding.ATW_EINVAL
     bad = binding._arr64([0, 0, 3])   # 3 bf16 elements = 6 bytes: not 16-byte multiple
     assert lib.atw_prefill(fake, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, None, 128, bad, s, s, s, 1e4,
-                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EUNSUPPORTED
+                           4.0, 1, 1, 0.0, fake, 1 << 40, None) == atw.binding.ATW_EUNSUPPORTED
     hmap = binding._arr32([0, 1, 2, 0])  # kv head 2 does not exist
     assert lib.atw_prefill(fake, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, hmap, 128, s, s, s, s, 1e4,
-                           4.0, 1, 1, 0.0, None) == atw.binding.ATW_EINVAL
+                           4.0, 1, 1, 0.0, fake, 1 << 40, None) == atw.binding.ATW_EINVAL
+    # workspace: bf16 needs one packed copy of K and V (64-key tiles), fp32 none
+    need = lib.atw_prefill_workspace_bytes(1, 1, 2, 10, 128)
+    assert need == 2 * 1 * 2 * 1 * 64 * 128 * 2
+    assert lib.atw_prefill_workspace_bytes(0, 1, 2, 10, 128) == 0
+    assert pre(ws=need - 1) == atw.binding.ATW_EWORKSPACE
 
 
 def test_decode_invalid_arguments(lib):
