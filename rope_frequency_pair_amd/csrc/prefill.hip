@@ -328,15 +328,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       // next k-step are read from LDS while the current one multiplies
       const int kk0 = r_full >> 3;
       if (kk0 < C::NKS) {
-        bf16x8 na0 = kop(C::NKS - 1, 0), na1 = kop(C::NKS - 1, 1);
+        // the K' operand blocks are read in two halves of k-steps, each half
+        // with no branch in between (a block of a pruned k-step holds stale
+        // data that is never used), so each MFMA waits only for its reads
+        constexpr int HALF = C::NKS / 2;
+        bf16x8 ka[C::NKS][2];
+#pragma unroll
+        for (int ks = C::NKS - 1; ks >= HALF; --ks) {
+          ka[ks][0] = kop(ks, 0);
+          ka[ks][1] = kop(ks, 1);
+        }
 #pragma unroll
         for (int ks = C::NKS - 1; ks >= 0; --ks) {
           if (ks < kk0) break;
-          const bf16x8 a0 = na0, a1 = na1;
-          if (ks > kk0) {
-            na0 = kop(ks - 1, 0);
-            na1 = kop(ks - 1, 1);
+          if (ks == HALF - 1) {
+#pragma unroll
+            for (int k2 = HALF - 1; k2 >= 0; --k2) {
+              ka[k2][0] = kop(k2, 0);
+              ka[k2][1] = kop(k2, 1);
+            }
           }
+          const bf16x8 a0 = ka[ks][0], a1 = ka[ks][1];
           u32x4 bw = __builtin_bit_cast(u32x4, qop[ks]);
           if (ks == kk0 && (r_full & 7)) {   // pairs below r_full of this k-step are partial
 #pragma unroll

@@ -22,7 +22,9 @@ import sys
 
 
 def _short(name, width=60):
-    name = name.split("(")[0] if name.startswith("void ") else name
+    if name.startswith("void "):
+        name = name[5:].replace("(anonymous namespace)::", "")
+        name = name.split("(")[0]
     return name if len(name) <= width else name[:width - 3] + "..."
 
 
