@@ -59,6 +59,22 @@ def prefill_flops(atw, n, d, h_q, batch, base, k_turns, window_on):
     return per_head_alg * h_q * batch, per_head_dense * h_q * batch, pruned / total
 
 
+def request_prefill_flops(atw, w):
+    """Algorithmic and dense-equivalent flops of the whole request's chunked
+    prefill (sum over chunks) and its pruned share."""
+    h = w.head_dim // 2
+    fo = fd = pr_all = tot_all = 0
+    for c in range(w.n // w.chunk):
+        pruned, total = atw.pruned_terms(w.chunk, (c + 1) * w.chunk, c * w.chunk, w.head_dim, w.rope_base,
+                                         w.k_turns, True, True)
+        cells = total // h
+        fo += (2 * w.head_dim * cells + 4 * (total - pruned)) * w.h_q * w.batch
+        fd += 4 * w.head_dim * cells * w.h_q * w.batch
+        pr_all += pruned
+        tot_all += total
+    return fo, fd, pr_all / tot_all
+
+
 def decode_bytes(atw, L, d, h_kv, batch, base, k_turns, window_on):
     """Algorithmic HBM bytes of one decode step: retained K pair slices
     (2 bytes per element, exact per-key window) + all of V, per kv head."""
@@ -339,6 +355,42 @@ def main():
             "on_vs_row_layout_off": round(result["decode_512k"]["ms_off"] / ma, 3),
             "line_bytes_on": by_line}
         del qd, kb, vc
+        torch.cuda.empty_cache()
+
+        # whole request, Qwen2.5-7B-1M shape: 16 x 64K chunked prefill + 128 decode steps
+        from rope_frequency_pair_amd import request as req
+        wr = synth.WORKLOADS["qwen2.5-7b-1m-request-1m"]
+        log(f"[bench] {wr.name}")
+        qr, qdr, kr, vr = synth.request_inputs(wr)
+        bufs = req.RequestBuffers(wr)
+        times = {}
+        for on in (True, False):
+            marks = []
+
+            def mark(c, _out):
+                if c == wr.n // wr.chunk - 1:
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record(stream)
+                    marks.append(ev)
+
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            req.run_request(wr, qr, qdr, kr, vr, bufs, window_on=on, on_chunk=mark)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[on] = (e0.elapsed_time(e1), e0.elapsed_time(marks[0]))
+            log(f"[bench] request window_on={on}: {times[on][0]:.1f} ms")
+        fo, fd, sh = request_prefill_flops(atw, wr)
+        result["request_1m"] = {
+            "ms_on": round(times[True][0], 1), "ms_off": round(times[False][0], 1),
+            "on_off_speedup": round(times[False][0] / times[True][0], 3),
+            "prefill_ms_on": round(times[True][1], 1), "prefill_ms_off": round(times[False][1], 1),
+            "decode_ms_on": round(times[True][0] - times[True][1], 2),
+            "decode_ms_off": round(times[False][0] - times[False][1], 2),
+            "prefill_tflops_algorithmic_on": round(fo / (times[True][1] * 1e-3) / 1e12, 1),
+            "prefill_pruned_share": round(sh, 4)}
+        del qr, qdr, kr, vr, bufs
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

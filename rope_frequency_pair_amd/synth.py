@@ -92,3 +92,22 @@ def workload_prefill_inputs(w, device="cuda", n=None):
 
 def workload_decode_inputs(w, device="cuda"):
     return decode_inputs(w.batch, w.h_q, w.h_kv, w.n, w.head_dim, w.dtype, w.seed, device, device)
+
+
+def request_inputs(w, device="cuda"):
+    """Inputs of the whole-request workload: q [B, Hq, N, d] of the prompt,
+    q_dec [steps, B, Hq, d] of the decode steps, and the caches k, v
+    [B, Hkv, N + steps, d] (token N + s is the key / value the decode step s
+    appends).  Drawn on the device generator in the order q, q_dec, k, v,
+    per kv head for the caches."""
+    g = generator(w.seed, device)
+    n_all = w.n + w.decode_steps
+    q = _randn((w.batch, w.h_q, w.n, w.head_dim), g, device, w.dtype)
+    q_dec = _randn((w.decode_steps, w.batch, w.h_q, w.head_dim), g, device, w.dtype)
+    k = torch.empty((w.batch, w.h_kv, n_all, w.head_dim), dtype=w.dtype, device=device)
+    v = torch.empty((w.batch, w.h_kv, n_all, w.head_dim), dtype=w.dtype, device=device)
+    for h in range(w.h_kv):
+        k[:, h] = _randn((w.batch, n_all, w.head_dim), g, device, w.dtype)
+    for h in range(w.h_kv):
+        v[:, h] = _randn((w.batch, n_all, w.head_dim), g, device, w.dtype)
+    return q, q_dec, k, v
