@@ -152,6 +152,23 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
   }
 }
 
+// Smallest / largest distance over the visible cells of query positions
+// [n_lo, n_hi] x key positions [m_lo, m_hi] (all below 2^30, so every
+// difference fits in int32); false if no cell is visible.
+__device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, bool causal,
+                                       int* dmin, int* dmax) {
+  if (n_hi < n_lo || m_hi < m_lo) return false;
+  if (causal) {
+    if (m_lo > n_hi) return false;
+    *dmin = max(n_lo - m_hi, 0);
+    *dmax = n_hi - m_lo;
+  } else {
+    *dmin = m_hi < n_lo ? n_lo - m_hi : (m_lo > n_hi ? m_lo - n_hi : 0);
+    *dmax = max(abs(n_hi - m_lo), abs(n_lo - m_hi));
+  }
+  return true;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillParams p) {
   using C = PCfg<D>;
@@ -159,10 +176,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   constexpr int TILE = kTK * D;
   __shared__ __attribute__((aligned(16))) __bf16 lk[2][TILE];
   __shared__ __attribute__((aligned(16))) __bf16 lv[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lq[kWaves][C::NKS * 512];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sh = lane >> 5, l32 = lane & 31;
-  const int grp = wave >> 2;   // 0: waves 0-3, 1: waves 4-7 (one phase later)
 
   // ---- work item.  The list (batch, kv head, query block descending, query
   // head) is mapped onto the XCDs (XCD x runs workgroups x, x+8, ...):
@@ -217,7 +235,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
 
   // ---- query: load, rotate at its position, keep as MFMA operand (lane l:
-  // query l%32, pairs 8ks + 4(l/32) + u as (x_r, x_{r+h}) pairs)
+  // query l%32, pairs 8ks + 4(l/32) + u as (x_r, x_{r+h}) pairs), in
+  // registers and in a per-wave LDS copy (read at a k-step chosen at run time)
+  __bf16* qw_lds = &lq[wave][0];
   const __bf16* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
   bf16x8 qop[C::NKS];
 #pragma unroll
@@ -235,6 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
     }
     qop[ks] = __builtin_bit_cast(bf16x8, packed);
+    *reinterpret_cast<u32x4*>(qw_lds + blk_off(ks, lane)) = packed;
   }
 
   f32x16 oacc[C::ND];
@@ -245,61 +266,63 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int kv_end = causal ? min(n_kv, gn_hi + 1) : n_kv;
   const int n_kt = (kv_end + kTK - 1) / kTK;
 
-  // ---- staging: wave w copies K' blocks w + 8i and V blocks w + 8i
+  // ---- staging (global -> registers -> LDS), one tile ahead: while tile t
+  // is worked from LDS buffer t & 1, tile t+1 (loaded during tile t-1) is
+  // written to the other buffer and tile t+2 is loaded.  Wave w copies K'
+  // blocks w + 8i and V blocks w + 8i.  A K' block of a k-step that the window
+  // drops for every cell of the workgroup is not fetched: its load re-reads
+  // the wave's first V block of the tile (already on its way through the
+  // caches) and what lands in its LDS slot is never read.  Every load and
+  // write is unconditional, so no staging register is ever merged between
+  // paths.
   // First k-step any cell of the workgroup needs in key tile t (wave-uniform).
   auto stage_ks = [&](int t) -> int {
     const int m_lo = t * kTK;
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
-    int64_t dmin = 0, dmax = 0;
-    if (!tile_distance_range(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return C::NKS;
+    int dmin = 0, dmax = 0;
+    if (!span32(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return C::NKS;
     return wave_pairs_below(w_lane, dmin) >> 3;
   };
   u32x4 kreg[C::KPW], vreg[C::VPW];
-  int pend_ks = 0;   // stage_ks of the tile held in kreg / vreg
   auto load = [&](int t) {
-    pend_ks = stage_ks(t);
+    const int ks0 = stage_ks(t);
     const __bf16* ks = kpk + (int64_t)t * TILE;
     const __bf16* vs = vpk + (int64_t)t * TILE;
 #pragma unroll
-    for (int i = 0; i < C::KPW; ++i) {
-      const int blk = wave + kWaves * i;
-      if ((blk >> 1) >= pend_ks) kreg[i] = *reinterpret_cast<const u32x4*>(ks + blk_off(blk, lane));
-    }
-#pragma unroll
     for (int i = 0; i < C::VPW; ++i)
       vreg[i] = *reinterpret_cast<const u32x4*>(vs + blk_off(wave + kWaves * i, lane));
+#pragma unroll
+    for (int i = 0; i < C::KPW; ++i) {
+      const int blk = wave + kWaves * i;
+      const __bf16* src = ((blk >> 1) >= ks0) ? ks + blk_off(blk, lane) : vs + blk_off(wave, lane);
+      kreg[i] = *reinterpret_cast<const u32x4*>(src);
+    }
   };
   auto write = [&](int t) {
     __bf16* kd = &lk[t & 1][0];
     __bf16* vd = &lv[t & 1][0];
 #pragma unroll
-    for (int i = 0; i < C::KPW; ++i) {
-      const int blk = wave + kWaves * i;
-      if ((blk >> 1) >= pend_ks) *reinterpret_cast<u32x4*>(kd + blk_off(blk, lane)) = kreg[i];
-    }
+    for (int i = 0; i < C::KPW; ++i)
+      *reinterpret_cast<u32x4*>(kd + blk_off(wave + kWaves * i, lane)) = kreg[i];
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i)
       *reinterpret_cast<u32x4*>(vd + blk_off(wave + kWaves * i, lane)) = vreg[i];
   };
 
-  // ---- prologue: tile 0 by everyone; waves 4-7 also load tile 1
+  // ---- prologue: tile 0 in LDS, tile 1 in registers
   load(0);
   write(0);
-  if (grp == 1 && n_kt > 1) load(1);
+  if (n_kt > 1) load(1);
   __syncthreads();
 
   for (int t = 0; t < n_kt; ++t) {
-    if (grp == 0) {
-      if (t + 1 < n_kt) load(t + 1);
-    } else {
-      if (t + 1 < n_kt) write(t + 1);
-      if (t + 2 < n_kt) load(t + 2);
-    }
+    if (t + 1 < n_kt) write(t + 1);
+    if (t + 2 < n_kt) load(t + 2);
 
     const int m_lo = t * kTK;
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
-    int64_t dmin = 0, dmax = 0;
-    if (wave_rows && tile_distance_range(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
+    int dmin = 0, dmax = 0;
+    if (wave_rows && span32(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
       const int r_any = wave_pairs_below(w_lane, dmin);
       const int r_full = wave_pairs_below(w_lane, dmax);
       const int kbase_lane = m_lo + 4 * sh;
@@ -323,14 +346,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         return *reinterpret_cast<const bf16x8*>(kt + blk_off(2 * ks + blk, lane));
       };
 
-      // pairs kept for every cell: k-steps kk0..NKS-1, taken from the top so
-      // the first MFMA starts from a zero accumulator; the operands of the
-      // next k-step are read from LDS while the current one multiplies
+      // pairs kept for every cell: k-steps kk0..NKS-1.  k-step kk0 first,
+      // from zero, with its query operand read from the LDS copy and the
+      // pairs below r_full (partial) masked out; then the k-steps above it
+      // from the registers, from the top.  The K' operands of the upper half
+      // of the k-steps are read before the branches (a block of a pruned
+      // k-step holds stale data that is never used), the lower half once the
+      // loop reaches it, so each MFMA waits only for its own reads.
       const int kk0 = r_full >> 3;
       if (kk0 < C::NKS) {
-        // the K' operand blocks are read in two halves of k-steps, each half
-        // with no branch in between (a block of a pruned k-step holds stale
-        // data that is never used), so each MFMA waits only for its reads
         constexpr int HALF = C::NKS / 2;
         bf16x8 ka[C::NKS][2];
 #pragma unroll
@@ -338,31 +362,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           ka[ks][0] = kop(ks, 0);
           ka[ks][1] = kop(ks, 1);
         }
+        {
+          u32x4 bw = *reinterpret_cast<const u32x4*>(qw_lds + blk_off(kk0, lane));
+          const int tau = r_full - 8 * kk0 - 4 * sh;   // slots below tau are partial
 #pragma unroll
-        for (int ks = C::NKS - 1; ks >= 0; --ks) {
-          if (ks < kk0) break;
+          for (int u = 0; u < 4; ++u) bw[u] = (u < tau) ? 0u : bw[u];
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, f32x16{}, 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ks = C::NKS - 1; ks >= 1; --ks) {
+          if (ks <= kk0) break;
           if (ks == HALF - 1) {
 #pragma unroll
-            for (int k2 = HALF - 1; k2 >= 0; --k2) {
+            for (int k2 = HALF - 1; k2 >= 1; --k2) {
               ka[k2][0] = kop(k2, 0);
               ka[k2][1] = kop(k2, 1);
             }
           }
-          const bf16x8 a0 = ka[ks][0], a1 = ka[ks][1];
-          u32x4 bw = __builtin_bit_cast(u32x4, qop[ks]);
-          if (ks == kk0 && (r_full & 7)) {   // pairs below r_full of this k-step are partial
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              if (8 * ks + 4 * sh + d < r_full) bw[d] = 0u;
-          }
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-          if (ks == C::NKS - 1) {
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, f32x16{}, 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, f32x16{}, 0, 0, 0);
-          } else {
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
-          }
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
         }
       } else {
         sacc[0] = f32x16{};
@@ -453,7 +473,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       l_run += lsum;
     }
 
-    if (grp == 0 && t + 1 < n_kt) write(t + 1);
     __syncthreads();
   }
 
