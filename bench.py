@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--quick", action="store_true", help="headline prefill only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--on-only", action="store_true",
+                    help="profiling: window-on launches of the headline prefill only (no ON/OFF rounds)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -209,11 +211,13 @@ def main():
     value = flops_on / (ms_step * 1e-3) / 1e12
 
     # window ON vs OFF, interleaved, median of >= 6 rounds each
-    rounds = max(6, args.steps)
+    rounds = 0 if args.on_only else max(6, args.steps)
     on_ms, off_ms = [], []
     for _ in range(rounds):
         on_ms += time_launches(lambda: step(True), stream, 1)
         off_ms += time_launches(lambda: step(False), stream, 1)
+    if args.on_only:
+        on_ms, off_ms = launch_ms, launch_ms
     med_on, med_off = statistics.median(on_ms), statistics.median(off_ms)
     ceiling = 2.0 / (1.0 + (1.0 - share))
     result = {
@@ -253,10 +257,10 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(flops_on / (kern_ms * 1e-3) / 1e12, 1),
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(flops_on / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                          "traffic": traffic, "kernel": "prefill_kernel<bf16,128>",
+                          "traffic": traffic, "kernel": "prefill_bf16_kernel<128>",
                           "kernel_ms_mean": round(kern_ms, 3), "kernel_sha": sha}
 
-    if not args.quick:
+    if not (args.quick or args.on_only):
         # ON/OFF sweep for "ON beats OFF at every context >= 32K"
         sweep = {}
         for n in (32768, 65536):

@@ -2,10 +2,15 @@
 
     python -m rope_frequency_pair_amd.rocprof_summary stats <run_results.db>
     python -m rope_frequency_pair_amd.rocprof_summary counters <run_results.db> [<db> ...]
+    python -m rope_frequency_pair_amd.rocprof_summary dispatches <run_results.db> \
+        [--kernel SUBSTR] [--skip N] [--first N]
     python -m rope_frequency_pair_amd.rocprof_summary traffic --fetch <db> --write <db> \
         --kernel prefill_kernel --copy-bytes 1073741824 --sha <kernel sha> --out <json>
 
 ``stats`` prints per-kernel call counts and durations (the --stats summary);
+``dispatches`` groups the dispatches of each kernel by launch grid, in launch
+order (optionally skipping the first N of a group and keeping the next M), so
+one workload's launches can be read apart from the others';
 ``counters`` prints the mean per-dispatch value of every collected counter
 per kernel; ``traffic`` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a
 kernel into bytes, scaled by what the same counters read for the plain device
@@ -56,6 +61,36 @@ def counters(db):
     return out
 
 
+def dispatch_groups(db, kernel=None, skip=0, first=None):
+    con = sqlite3.connect(db)
+    groups = collections.OrderedDict()
+    for name, dur, gx, gy, gz, wx in con.execute(
+            "select name, duration, grid_x, grid_y, grid_z, workgroup_x from kernels order by start"):
+        if kernel and kernel not in name:
+            continue
+        groups.setdefault((name, gx, gy, gz, wx), []).append(dur)
+    out = []
+    for (name, gx, gy, gz, wx), d in groups.items():
+        d = d[skip:]
+        if first is not None:
+            d = d[:first]
+        if d:
+            out.append({"name": name, "grid": (gx, gy, gz), "wg": wx, "calls": len(d),
+                        "avg_ns": statistics.mean(d), "min_ns": min(d), "max_ns": max(d)})
+    return out
+
+
+def _print_dispatches(db, kernel, skip, first):
+    print(f"dispatches grouped by launch grid, from {db}" + (f" (skip {skip}, first {first})" if skip or first else ""))
+    print()
+    print("| kernel | grid (threads) | workgroup | calls | avg (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|---|")
+    for r in dispatch_groups(db, kernel, skip, first):
+        g = "x".join(str(x) for x in r["grid"])
+        print(f"| {_short(r['name'])} | {g} | {r['wg']} | {r['calls']} | {r['avg_ns'] / 1e3:.1f} | "
+              f"{r['min_ns'] / 1e3:.1f} | {r['max_ns'] / 1e3:.1f} |")
+
+
 def _print_stats(db):
     print(f"kernel statistics from {db}\n")
     print("| kernel | calls | avg (us) | min (us) | max (us) | total (ms) |")
@@ -102,6 +137,11 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("db")
+    dsp = sub.add_parser("dispatches")
+    dsp.add_argument("db")
+    dsp.add_argument("--kernel", default=None)
+    dsp.add_argument("--skip", type=int, default=0)
+    dsp.add_argument("--first", type=int, default=None)
     c = sub.add_parser("counters")
     c.add_argument("db", nargs="+")
     t = sub.add_parser("traffic")
@@ -115,6 +155,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         _print_stats(a.db)
+    elif a.cmd == "dispatches":
+        _print_dispatches(a.db, a.kernel, a.skip, a.first)
     elif a.cmd == "counters":
         _print_counters(a.db)
     else:
