@@ -281,7 +281,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 only");
   if (batch <= 0 || batch > atw::kMaxDecodeBatch)
     return fail(ATW_EUNSUPPORTED, "batch must be in 1..%d", atw::kMaxDecodeBatch);
-  if (num_splits <= 0 || num_splits > 1024) return fail(ATW_EINVAL, "num_splits must be in 1..1024");
+  if (num_splits <= 0 || num_splits > atw::kMaxDecodeSplits)
+    return fail(ATW_EINVAL, "num_splits must be in 1..%d", atw::kMaxDecodeSplits);
   if (!std::isfinite(softmax_scale)) return fail(ATW_EINVAL, "softmax_scale must be finite");
   if (kv_len == nullptr || q_pos == nullptr) return fail(ATW_EINVAL, "kv_len and q_pos must be non-NULL");
   for (int64_t b = 0; b < batch; ++b) {

@@ -35,6 +35,7 @@ struct PrefillParams {
 
 // Decode: split-KV over the key axis, then a combine pass.
 constexpr int kDecodeTileK = 64;
+constexpr int kMaxDecodeSplits = 1024;
 
 struct DecodeParams {
   const void* q;
