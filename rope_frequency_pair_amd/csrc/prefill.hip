@@ -47,6 +47,10 @@
 //    one workgroup barrier per tile;
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
+//  * head_dim 64 asks for four waves per SIMD (two workgroups per CU: 64 KB
+//    of LDS and at most 128 registers each); its full k-steps read their
+//    operands per k-step and the query operand from the LDS copy, which keeps
+//    the hot path free of register spills at that budget.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -170,7 +174,7 @@ __device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, b
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel(const PrefillParams p) {
   using C = PCfg<D>;
   constexpr int H = C::H;
   constexpr int TILE = kTK * D;
@@ -357,10 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       if (kk0 < C::NKS) {
         constexpr int HALF = C::NKS / 2;
         bf16x8 ka[C::NKS][2];
+        if constexpr (D != 64) {
 #pragma unroll
-        for (int ks = C::NKS - 1; ks >= HALF; --ks) {
-          ka[ks][0] = kop(ks, 0);
-          ka[ks][1] = kop(ks, 1);
+          for (int ks = C::NKS - 1; ks >= HALF; --ks) {
+            ka[ks][0] = kop(ks, 0);
+            ka[ks][1] = kop(ks, 1);
+          }
         }
         {
           u32x4 bw = *reinterpret_cast<const u32x4*>(qw_lds + blk_off(kk0, lane));
@@ -371,18 +377,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, f32x16{}, 0, 0, 0);
           sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
         }
+        if constexpr (D == 64) {
+          // head_dim 64: operands read per k-step, query operand from the LDS
+          // copy, so that two workgroups fit on a CU (registers)
 #pragma unroll
-        for (int ks = C::NKS - 1; ks >= 1; --ks) {
-          if (ks <= kk0) break;
-          if (ks == HALF - 1) {
-#pragma unroll
-            for (int k2 = HALF - 1; k2 >= 1; --k2) {
-              ka[k2][0] = kop(k2, 0);
-              ka[k2][1] = kop(k2, 1);
-            }
+          for (int ks = C::NKS - 1; ks >= 1; --ks) {
+            if (ks <= kk0) break;
+            const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qw_lds + blk_off(ks, lane));
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(ks, 0), qb, sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(ks, 1), qb, sacc[1], 0, 0, 0);
           }
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int ks = C::NKS - 1; ks >= 1; --ks) {
+            if (ks <= kk0) break;
+            if (ks == HALF - 1) {
+  #pragma unroll
+              for (int k2 = HALF - 1; k2 >= 1; --k2) {
+                ka[k2][0] = kop(k2, 0);
+                ka[k2][1] = kop(k2, 1);
+              }
+            }
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
+          }
         }
       } else {
         sacc[0] = f32x16{};
@@ -395,13 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         for (int pp = r_any; pp < r_full; ++pp) {
           const int ks = pp >> 3, uu = pp & 7;
           const bf16x8 a0 = kop(ks, 0), a1 = kop(ks, 1);
-          uint32_t qd = 0u;
-#pragma unroll
-          for (int k2 = 0; k2 < C::NKS; ++k2) {
-            const u32x4 qw = __builtin_bit_cast(u32x4, qop[k2]);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) qd = (k2 == ks && d == (uu & 3)) ? qw[d] : qd;
-          }
+          const uint32_t qd =
+              *reinterpret_cast<const uint32_t*>(qw_lds + blk_off(ks, lane) + 2 * (uu & 3));
           const bool mine = sh == (uu >> 2);
           u32x4 bw;
 #pragma unroll
