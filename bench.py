@@ -48,9 +48,14 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
-def prefill_flops(atw, n, d, h_q, batch, base, k_turns, window_on):
+# rope_scaling of the Llama-3.2-3B config (llama3 rule)
+LLAMA32_SCALING = {"rope_type": "llama3", "factor": 32.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+                   "original_max_position_embeddings": 8192}
+
+
+def prefill_flops(atw, n, d, h_q, batch, base, k_turns, window_on, rope_scaling=None):
     """(algorithmic, dense-equivalent) flops of one causal prefill of length n."""
-    pruned, total = atw.pruned_terms(n, n, 0, d, base, k_turns, True, window_on)
+    pruned, total = atw.pruned_terms(n, n, 0, d, base, k_turns, True, window_on, rope_scaling)
     h = d // 2
     cells = total // h
     retained = total - pruned
@@ -192,8 +197,9 @@ def main():
     q, k, v = synth.workload_prefill_inputs(w)
     out = torch.empty_like(q)
 
-    def step(on=True, qq=q, kk=k, vv=v, oo=out, wl=w):
-        atw.prefill(qq, kk, vv, rope_base=wl.rope_base, k_turns=wl.k_turns, window_on=on, out=oo)
+    def step(on=True, qq=q, kk=k, vv=v, oo=out, wl=w, sc=None):
+        atw.prefill(qq, kk, vv, rope_base=wl.rope_base, k_turns=wl.k_turns, window_on=on, out=oo,
+                    rope_scaling=sc)
 
     flops_on, dense, share = prefill_flops(atw, w.n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, True)
     flops_off, _, _ = prefill_flops(atw, w.n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, False)
@@ -276,6 +282,21 @@ def main():
                              "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
                              "pruned_share": round(sh, 4)}
         result["prefill_llama_sweep"] = sweep
+
+        # the same 128K step with the model's own rope scaling (llama3 rule): the
+        # windows come from the rescaled wavelengths
+        a, b = [], []
+        for _ in range(6):
+            a += time_launches(lambda: step(True, sc=LLAMA32_SCALING), stream, 1)
+            b += time_launches(lambda: step(False, sc=LLAMA32_SCALING), stream, 1)
+        fo, _, sh = prefill_flops(atw, w.n, w.head_dim, w.h_q, w.batch, w.rope_base, w.k_turns, True,
+                                  LLAMA32_SCALING)
+        result["prefill_128k_llama3_scaling"] = {
+            "rope_scaling": LLAMA32_SCALING, "pruned_share": round(sh, 4),
+            "ms_on": round(statistics.median(a), 3), "ms_off": round(statistics.median(b), 3),
+            "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+            "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
+            "ceiling_2_over_1_plus_s": round(2.0 / (2.0 - sh), 3)}
         del q, k, v, out
         torch.cuda.empty_cache()
 

@@ -68,6 +68,89 @@ extern "C" {
 #define ATW_UNBOUNDED ((int64_t)1 << 62)
 
 /*
+ * RoPE frequencies of a model whose config rescales them.  The window tables
+ * are built from the RoPE base, the head dimension and the model's
+ * rope_scaling ("ATFlash — Per-RoPE-Wavelength Attention Windows", README,
+ * "Using the ports"); the rotation and the windows both use the rescaled
+ * theta_r, so the window of pair r is w_r = k * 2*pi / theta_r.  The
+ * *_rope entry points take this descriptor (host memory, read during the
+ * call only) in place of rope_base; the others use ATW_ROPE_PLAIN.
+ *
+ *   ATW_ROPE_PLAIN   theta_r = base^(-2r/d).
+ *   ATW_ROPE_LINEAR  the plain theta_r divided by factor (position
+ *                    interpolation).
+ *   ATW_ROPE_LLAMA3  with L = original_max_position and the plain
+ *                    wavelength lambda_r = 2*pi/theta_r: pairs with
+ *                    lambda_r < L / high_freq_factor keep theta_r, pairs with
+ *                    lambda_r > L / low_freq_factor get theta_r / factor, and
+ *                    in between theta_r' = (1 - s) theta_r / factor + s theta_r
+ *                    with s = (L / lambda_r - low_freq_factor) /
+ *                    (high_freq_factor - low_freq_factor) (the frequency rule
+ *                    of the Llama 3.1 / 3.2 model configs).
+ *   ATW_ROPE_TABLE   theta_r given per pair in theta[0 .. d/2 - 1] (any other
+ *                    rescaling rule, computed by the caller).
+ *
+ * Every resulting theta_r must be finite, > 0 and non-increasing in r (then
+ * the windows grow with r and the kept pairs at any distance are a suffix);
+ * otherwise the call returns ATW_EINVAL.
+ */
+#define ATW_ROPE_PLAIN 0
+#define ATW_ROPE_LINEAR 1
+#define ATW_ROPE_LLAMA3 2
+#define ATW_ROPE_TABLE 3
+
+typedef struct atw_rope {
+  int32_t kind;                 /* ATW_ROPE_* */
+  int32_t reserved;             /* 0 */
+  double base;                  /* PLAIN, LINEAR, LLAMA3: > 1 */
+  double factor;                /* LINEAR, LLAMA3: > 0 */
+  double low_freq_factor;       /* LLAMA3: > 0 */
+  double high_freq_factor;      /* LLAMA3: > low_freq_factor */
+  double original_max_position; /* LLAMA3: > 0 */
+  const double* theta;          /* TABLE: d/2 frequencies (host) */
+} atw_rope;
+
+/* theta_r of every pair of a descriptor (d/2 values, host) -- host only. */
+int atw_rope_theta(const atw_rope* rope, int32_t head_dim, double* theta_out);
+
+/* atw_window_widths with a RoPE descriptor -- host only. */
+int atw_window_widths_rope(const atw_rope* rope, int32_t head_dim, double k_turns,
+                           int32_t window_on, int64_t* widths_out);
+
+/* atw_pruned_terms with a RoPE descriptor -- host only. */
+int atw_pruned_terms_rope(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim,
+                          const atw_rope* rope, double k_turns, int32_t causal, int32_t window_on,
+                          int64_t* pruned, int64_t* total);
+
+/* atw_prefill with a RoPE descriptor in place of rope_base (every other
+ * argument, the result and the limits as for atw_prefill). */
+int atw_prefill_rope(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                     int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q,
+                     int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                     const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                     int32_t window_on, double softmax_scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* atw_decode / atw_decode_banded with a RoPE descriptor in place of rope_base. */
+int atw_decode_rope(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                    int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                    int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                    const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                    const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                    int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cache, void* o,
+                           int32_t dtype, int64_t batch, const int64_t* kv_len,
+                           const int64_t* q_pos, int32_t h_q, int32_t h_kv,
+                           const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
+                           const int64_t* k_strides, const int64_t* v_strides,
+                           const int64_t* o_strides, const atw_rope* rope, double k_turns,
+                           int32_t causal, int32_t window_on, double softmax_scale,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * atw_prefill -- windowed causal (or non-causal) attention for a block of
  * queries against a key/value sequence ("The idea": the window is a slice of
  * the query-key contraction axis; "Porting to something else": the pair loop

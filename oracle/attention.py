@@ -72,11 +72,11 @@ def _row_output(q_hat, q_pos, k_hat, v, k_pos, widths, scale, causal):
 
 
 def windowed_scores(q, k, q_positions, k_positions, head_dim, rope_base, k_turns,
-                    window_on=True, causal=True, scale=None):
+                    window_on=True, causal=True, scale=None, scaling=None):
     """Scores s[P, M] of one head for queries q[P, d] at q_positions and keys
     k[M, d] at k_positions; invisible cells are -inf."""
-    theta = pair_frequencies(head_dim, rope_base)
-    widths = window_widths(head_dim, rope_base, k_turns, window_on)
+    theta = pair_frequencies(head_dim, rope_base, scaling)
+    widths = window_widths(head_dim, rope_base, k_turns, window_on, scaling)
     scale = 1.0 / math.sqrt(head_dim) if scale is None or scale <= 0 else scale
     qp = np.asarray(q_positions, dtype=np.int64)
     kp = np.asarray(k_positions, dtype=np.int64)
@@ -106,7 +106,7 @@ def _head_map(h_q, h_kv, kv_head_of_q):
 
 
 def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, scale=None,
-            kv_head_of_q=None, query_rows=None, heads=None, batches=None):
+            kv_head_of_q=None, query_rows=None, heads=None, batches=None, scaling=None):
     """Windowed attention output for prefill, float64.
 
     q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nkv, d] (pre-RoPE).  Returns
@@ -118,8 +118,8 @@ def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, sc
     bsz, h_q, n_q, d = q.shape
     h_kv, n_kv = k.shape[1], k.shape[2]
     hmap = _head_map(h_q, h_kv, kv_head_of_q)
-    theta = pair_frequencies(d, rope_base)
-    widths = window_widths(d, rope_base, k_turns, window_on)
+    theta = pair_frequencies(d, rope_base, scaling)
+    widths = window_widths(d, rope_base, k_turns, window_on, scaling)
     scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else scale
     rows = np.arange(n_q) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
     heads = list(range(h_q)) if heads is None else list(heads)
@@ -145,7 +145,7 @@ def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, sc
 
 
 def decode(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal=True, window_on=True,
-           scale=None, kv_head_of_q=None, heads=None, batches=None):
+           scale=None, kv_head_of_q=None, heads=None, batches=None, scaling=None):
     """Windowed attention output for single-token decode, float64.
 
     q: [B, Hq, d] (pre-RoPE, query of batch b at position q_pos[b]);
@@ -156,8 +156,8 @@ def decode(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal=True, 
     bsz, h_q, d = q.shape
     h_kv = k_cache.shape[1]
     hmap = _head_map(h_q, h_kv, kv_head_of_q)
-    theta = pair_frequencies(d, rope_base)
-    widths = window_widths(d, rope_base, k_turns, window_on)
+    theta = pair_frequencies(d, rope_base, scaling)
+    widths = window_widths(d, rope_base, k_turns, window_on, scaling)
     scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else scale
     heads = list(range(h_q)) if heads is None else list(heads)
     batches = list(range(bsz)) if batches is None else list(batches)

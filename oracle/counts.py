@@ -30,7 +30,8 @@ import numpy as np
 from .window import window_widths, visible_cells
 
 
-def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, window_on=True):
+def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, window_on=True,
+                 scaling=None):
     """Exact (pruned, total) pair-term counts; per-row interval counting.
 
     Row n sees a contiguous set of distances; pair r is pruned on the part of
@@ -39,7 +40,7 @@ def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, w
     h = head_dim // 2
     if n_q <= 0 or n_kv <= 0:
         return 0, 0
-    widths = window_widths(head_dim, rope_base, k_turns, window_on)
+    widths = window_widths(head_dim, rope_base, k_turns, window_on, scaling)
     n = q_pos0 + np.arange(n_q, dtype=np.int64)
     pruned = 0
     if causal:
@@ -62,7 +63,7 @@ def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, w
 
 
 def pruned_terms_bruteforce(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True,
-                            window_on=True):
+                            window_on=True, scaling=None):
     """Exact counts by enumerating every visible (query, key, pair) triple.
 
     Only for small sizes (materialises the n_q x n_kv cell grid).
@@ -70,7 +71,7 @@ def pruned_terms_bruteforce(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, cau
     h = head_dim // 2
     if n_q <= 0 or n_kv <= 0:
         return 0, 0
-    widths = window_widths(head_dim, rope_base, k_turns, window_on)
+    widths = window_widths(head_dim, rope_base, k_turns, window_on, scaling)
     vis, dist = visible_cells(n_q, n_kv, q_pos0, causal)
     d = dist[vis]
     pruned = 0

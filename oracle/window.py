@@ -19,6 +19,20 @@ Readings (the pages leave these open):
 * window off, or ``k = +inf``, means every term is kept: ``W_r = UNBOUNDED``;
 * ``W_r`` is clamped to ``UNBOUNDED = 2**62`` so it stays an int64.
 
+Rescaled frequencies ("Using the ports": the window tables are built from the
+RoPE base, the head dim and the model's rope_scaling; the pages name
+rope_scaling but do not define any rule).  Reading: the rotation and the
+windows both use the model's rescaled theta_r, and a ``scaling`` dict gives
+the rule in the style of a model config:
+
+* ``{"rope_type": "linear", "factor": f}``: every theta_r divided by f;
+* ``{"rope_type": "llama3", "factor": f, "low_freq_factor": a,
+  "high_freq_factor": b, "original_max_position_embeddings": L}``: the rule of
+  the Llama 3.1 / 3.2 configs -- with the plain wavelength lambda_r, a pair
+  keeps theta_r when lambda_r < L/b, gets theta_r/f when lambda_r > L/a, and in
+  between the blend (1 - s) theta_r/f + s theta_r, s = (L/lambda_r - a)/(b - a);
+* ``{"rope_type": "table", "theta": [...]}``: theta_r given per pair.
+
 "Porting to something else" asks for the retained prefix per key tile; here a
 tile plan gives, per (query tile, key tile), the first pair needed by some
 visible cell (``r_any``) and the first pair needed by every visible cell
@@ -32,20 +46,50 @@ import numpy as np
 UNBOUNDED = 1 << 62
 
 
-def pair_frequencies(head_dim, rope_base):
-    """theta_r = base**(-2r/d) for r = 0..d/2-1, float64 ("The idea")."""
+def pair_frequencies(head_dim, rope_base, scaling=None):
+    """theta_r = base**(-2r/d) for r = 0..d/2-1, float64 ("The idea"),
+    rescaled by the model's rope scaling rule when ``scaling`` is given."""
     if head_dim <= 0 or head_dim % 2:
         raise ValueError("head_dim must be a positive even integer")
-    r = np.arange(head_dim // 2, dtype=np.float64)
-    return np.power(np.float64(rope_base), -2.0 * r / head_dim)
+    h = head_dim // 2
+    if scaling is not None and scaling.get("rope_type", scaling.get("type")) == "table":
+        theta = np.array([float(x) for x in scaling["theta"]], dtype=np.float64)
+        if theta.shape != (h,):
+            raise ValueError("a frequency table needs head_dim/2 entries")
+        return theta
+    r = np.arange(h, dtype=np.float64)
+    theta = np.power(np.float64(rope_base), -2.0 * r / head_dim)
+    if scaling is None:
+        return theta
+    kind = scaling.get("rope_type", scaling.get("type"))
+    if kind == "linear":
+        return theta / np.float64(scaling["factor"])
+    if kind == "llama3":
+        f = float(scaling["factor"])
+        a = float(scaling["low_freq_factor"])
+        b = float(scaling["high_freq_factor"])
+        L = float(scaling.get("original_max_position_embeddings", scaling.get("original_max_position")))
+        out = np.empty(h, dtype=np.float64)
+        for i in range(h):
+            t = float(theta[i])
+            lam = 2.0 * math.pi / t           # plain wavelength of the pair
+            if lam < L / b:                   # short wavelengths: unchanged
+                out[i] = t
+            elif lam > L / a:                 # long wavelengths: interpolated by f
+                out[i] = t / f
+            else:                             # in between: blend of the two
+                s_ = (L / lam - a) / (b - a)
+                out[i] = (1.0 - s_) * t / f + s_ * t
+        return out
+    raise ValueError(f"unknown rope scaling type {kind!r}")
 
 
-def pair_wavelengths(head_dim, rope_base):
+def pair_wavelengths(head_dim, rope_base, scaling=None):
     """lambda_r = 2*pi / theta_r: positions per full turn of pair r."""
-    return (2.0 * math.pi) / pair_frequencies(head_dim, rope_base)
+    return (2.0 * math.pi) / pair_frequencies(head_dim, rope_base, scaling)
 
 
-def window_widths(head_dim, rope_base, k_turns, window_on=True):
+def window_widths(head_dim, rope_base, k_turns, window_on=True, scaling=None):
     """Integer windows W_r = floor(k * lambda_r) as int64 (UNBOUNDED when off).
 
     Pair r's term is kept at integer distance delta iff delta <= W_r.
@@ -55,7 +99,7 @@ def window_widths(head_dim, rope_base, k_turns, window_on=True):
         return np.full(h, UNBOUNDED, dtype=np.int64)
     if not k_turns > 0:
         raise ValueError("k_turns must be > 0 when the window is on")
-    w = np.float64(k_turns) * pair_wavelengths(head_dim, rope_base)
+    w = np.float64(k_turns) * pair_wavelengths(head_dim, rope_base, scaling)
     w = np.floor(w)
     out = np.empty(h, dtype=np.int64)
     for r in range(h):

@@ -26,6 +26,8 @@ from .binding import (  # noqa: F401
     prefill,
     prefill_workspace_bytes,
     pruned_terms,
+    rope_descriptor,
+    rope_theta,
     version,
     window_plan,
     window_plan_device,

@@ -20,8 +20,53 @@ EXPORTED = [
     "atw_prefill", "atw_prefill_workspace_bytes", "atw_decode", "atw_decode_banded", "atw_kcache_band",
     "atw_decode_workspace_bytes", "atw_pruned_terms",
     "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
-    "atw_version",
+    "atw_version", "atw_rope_theta", "atw_window_widths_rope", "atw_pruned_terms_rope",
+    "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope",
 ]
+
+ATW_ROPE_PLAIN, ATW_ROPE_LINEAR, ATW_ROPE_LLAMA3, ATW_ROPE_TABLE = 0, 1, 2, 3
+
+
+class Rope(ctypes.Structure):
+    """Mirror of struct atw_rope (include/atw.h)."""
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("base", ctypes.c_double),
+                ("factor", ctypes.c_double), ("low_freq_factor", ctypes.c_double),
+                ("high_freq_factor", ctypes.c_double), ("original_max_position", ctypes.c_double),
+                ("theta", ctypes.POINTER(ctypes.c_double))]
+
+
+def rope_descriptor(rope_base, rope_scaling):
+    """atw_rope for a model's RoPE: rope_scaling None (plain) or a dict in the
+    style of a model config: {"rope_type": "linear", "factor": f},
+    {"rope_type": "llama3", "factor", "low_freq_factor", "high_freq_factor",
+    "original_max_position_embeddings"}, or {"rope_type": "table", "theta":
+    [theta_0, ...]} (explicit per-pair frequencies).  "type" is accepted for
+    "rope_type"."""
+    r = Rope()
+    r.base = float(rope_base) if rope_base is not None else 0.0
+    if rope_scaling is None:
+        r.kind = ATW_ROPE_PLAIN
+        return r
+    kind = rope_scaling.get("rope_type", rope_scaling.get("type"))
+    if kind == "linear":
+        r.kind = ATW_ROPE_LINEAR
+        r.factor = float(rope_scaling["factor"])
+    elif kind == "llama3":
+        r.kind = ATW_ROPE_LLAMA3
+        r.factor = float(rope_scaling["factor"])
+        r.low_freq_factor = float(rope_scaling["low_freq_factor"])
+        r.high_freq_factor = float(rope_scaling["high_freq_factor"])
+        r.original_max_position = float(rope_scaling.get("original_max_position_embeddings",
+                                                         rope_scaling.get("original_max_position")))
+    elif kind == "table":
+        vals = [float(x) for x in rope_scaling["theta"]]
+        buf = (ctypes.c_double * len(vals))(*vals)
+        r.kind = ATW_ROPE_TABLE
+        r.theta = ctypes.cast(buf, ctypes.POINTER(ctypes.c_double))
+        r._keep = buf
+    else:
+        raise ValueError(f"unknown rope_scaling type {kind!r}")
+    return r
 
 
 class AtwError(RuntimeError):
@@ -71,6 +116,19 @@ def load_library(path=LIB_PATH):
     lib.atw_window_plan_device.argtypes = [_i32, _f64, _f64, _i32, _i64, _i64, _i64, _i32, _i32, _i32,
                                            _vp, _vp, _vp]
     lib.atw_window_plan_device.restype = ctypes.c_int
+    _prope = ctypes.POINTER(Rope)
+    lib.atw_rope_theta.argtypes = [_prope, _i32, ctypes.POINTER(ctypes.c_double)]
+    lib.atw_rope_theta.restype = ctypes.c_int
+    lib.atw_window_widths_rope.argtypes = [_prope, _i32, _f64, _i32, _pi64]
+    lib.atw_window_widths_rope.restype = ctypes.c_int
+    lib.atw_pruned_terms_rope.argtypes = [_i64, _i64, _i64, _i32, _prope, _f64, _i32, _i32, _pi64, _pi64]
+    lib.atw_pruned_terms_rope.restype = ctypes.c_int
+    lib.atw_prefill_rope.argtypes = lib.atw_prefill.argtypes[:17] + [_prope] + lib.atw_prefill.argtypes[18:]
+    lib.atw_prefill_rope.restype = ctypes.c_int
+    lib.atw_decode_rope.argtypes = lib.atw_decode.argtypes[:16] + [_prope] + lib.atw_decode.argtypes[17:]
+    lib.atw_decode_rope.restype = ctypes.c_int
+    lib.atw_decode_banded_rope.argtypes = lib.atw_decode_rope.argtypes
+    lib.atw_decode_banded_rope.restype = ctypes.c_int
     lib.atw_last_error.argtypes = []
     lib.atw_last_error.restype = ctypes.c_char_p
     lib.atw_version.argtypes = []
@@ -119,20 +177,39 @@ def version():
     return load_library().atw_version().decode()
 
 
-def window_widths(head_dim, rope_base, k_turns, window_on=True):
+def window_widths(head_dim, rope_base, k_turns, window_on=True, rope_scaling=None):
     """Integer windows W_r (list of int) computed by the library."""
     lib = load_library()
     out = (ctypes.c_int64 * (head_dim // 2))()
-    _check(lib.atw_window_widths(head_dim, float(rope_base), float(k_turns), int(window_on), out))
+    if rope_scaling is None:
+        _check(lib.atw_window_widths(head_dim, float(rope_base), float(k_turns), int(window_on), out))
+    else:
+        r = rope_descriptor(rope_base, rope_scaling)
+        _check(lib.atw_window_widths_rope(ctypes.byref(r), head_dim, float(k_turns), int(window_on), out))
     return list(out)
 
 
-def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, window_on=True):
+def rope_theta(head_dim, rope_base, rope_scaling=None):
+    """theta_r of every pair (list of float) as the library computes them."""
+    lib = load_library()
+    out = (ctypes.c_double * (head_dim // 2))()
+    r = rope_descriptor(rope_base, rope_scaling)
+    _check(lib.atw_rope_theta(ctypes.byref(r), head_dim, out))
+    return list(out)
+
+
+def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, window_on=True,
+                 rope_scaling=None):
     """(pruned, total) pair-term counts per (batch, query head)."""
     lib = load_library()
     p, t = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib.atw_pruned_terms(n_q, n_kv, q_pos0, head_dim, float(rope_base), float(k_turns),
-                                int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
+    if rope_scaling is None:
+        _check(lib.atw_pruned_terms(n_q, n_kv, q_pos0, head_dim, float(rope_base), float(k_turns),
+                                    int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
+    else:
+        r = rope_descriptor(rope_base, rope_scaling)
+        _check(lib.atw_pruned_terms_rope(n_q, n_kv, q_pos0, head_dim, ctypes.byref(r), float(k_turns),
+                                         int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
     return p.value, t.value
 
 
@@ -170,7 +247,7 @@ def prefill_workspace_bytes(dtype_code, batch, h_kv, n_kv, head_dim):
 
 
 def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=True, scale=None,
-            kv_head_of_q=None, out=None, workspace=None, stream=None):
+            kv_head_of_q=None, out=None, workspace=None, stream=None, rope_scaling=None):
     """Windowed prefill.  q [B, Hq, Nq, d]; k, v [B, Hkv, Nkv, d] (any strides
     with d contiguous), bf16 or fp32 CUDA tensors.  Returns out [B, Hq, Nq, d].
     workspace: device buffer of prefill_workspace_bytes(...) bytes, allocated
@@ -189,11 +266,16 @@ def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=Tru
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.atw_prefill(
+    if rope_scaling is None:
+        entry, rope_arg = lib.atw_prefill, float(rope_base)
+    else:
+        rdesc = rope_descriptor(rope_base, rope_scaling)
+        entry, rope_arg = lib.atw_prefill_rope, ctypes.byref(rdesc)
+    _check(entry(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
         _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
-        _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), float(rope_base), float(k_turns),
+        _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), rope_arg, float(k_turns),
         int(causal), int(window_on), float(scale or 0.0), ws_ptr, ws_len, _stream_ptr(stream)))
     return out
 
@@ -203,22 +285,24 @@ def decode_workspace_bytes(batch, h_q, head_dim, num_splits):
 
 
 def decode(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=True, window_on=True,
-           scale=None, num_splits=64, kv_head_of_q=None, workspace=None, out=None, stream=None):
+           scale=None, num_splits=64, kv_head_of_q=None, workspace=None, out=None, stream=None,
+           rope_scaling=None):
     """Windowed split-KV decode.  q [B, Hq, d]; caches [B, Hkv, L, d] bf16 CUDA
     tensors; kv_len, q_pos: per-sequence ints.  Returns out [B, Hq, d]."""
     return _decode("atw_decode", q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal,
-                   window_on, scale, num_splits, kv_head_of_q, workspace, out, stream)
+                   window_on, scale, num_splits, kv_head_of_q, workspace, out, stream, rope_scaling)
 
 
 def decode_banded(q, k_bands, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=True,
                   window_on=True, scale=None, num_splits=64, kv_head_of_q=None, workspace=None,
-                  out=None, stream=None):
+                  out=None, stream=None, rope_scaling=None):
     """decode() over a pair-banded K cache k_bands [B, Hkv, d/16, L, 16] (token
     stride 16); v_cache [B, Hkv, L, d] as for decode()."""
     if k_bands.dim() != 5 or k_bands.shape[-1] != 16 or k_bands.stride(3) != 16:
         raise ValueError("k_bands must be [B, Hkv, d/16, L, 16] with token stride 16")
     return _decode("atw_decode_banded", q, k_bands, v_cache, kv_len, q_pos, rope_base, k_turns,
-                   causal, window_on, scale, num_splits, kv_head_of_q, workspace, out, stream)
+                   causal, window_on, scale, num_splits, kv_head_of_q, workspace, out, stream,
+                   rope_scaling)
 
 
 def kcache_band(k_rows, k_bands=None, *, t0=0, n_tokens=None, stream=None):
@@ -246,7 +330,7 @@ def kcache_band(k_rows, k_bands=None, *, t0=0, n_tokens=None, stream=None):
 
 
 def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal, window_on,
-            scale, num_splits, kv_head_of_q, workspace, out, stream):
+            scale, num_splits, kv_head_of_q, workspace, out, stream, rope_scaling=None):
     import torch
     lib = load_library()
     B, Hq, D = q.shape
@@ -258,12 +342,17 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
     q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
+    if rope_scaling is None:
+        rope_arg = float(rope_base)
+    else:
+        rdesc = rope_descriptor(rope_base, rope_scaling)
+        entry, rope_arg = entry + "_rope", ctypes.byref(rdesc)
     _check(getattr(lib, entry)(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
         ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
         _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
-        _arr64(out.stride()[:2]), float(rope_base), float(k_turns), int(causal), int(window_on),
+        _arr64(out.stride()[:2]), rope_arg, float(k_turns), int(causal), int(window_on),
         float(scale or 0.0), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return out

@@ -45,6 +45,51 @@ int check_window(int32_t head_dim, double rope_base, double k_turns, int32_t win
   return ATW_OK;
 }
 
+// Frequencies theta_r of a RoPE descriptor, after the head_dim / k checks.
+int resolve_rope(const atw_rope* rope, int32_t head_dim, double k_turns, int32_t window_on,
+                 int max_dim, double* theta) {
+  if (rope == nullptr) return fail(ATW_EINVAL, "rope is NULL");
+  if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > max_dim)
+    return fail(ATW_EINVAL, "head_dim must be even and in 2..%d (got %d)", max_dim, head_dim);
+  if (window_on && !(k_turns > 0.0))
+    return fail(ATW_EINVAL, "k_turns must be > 0 when the window is on (got %g)", k_turns);
+  atw::RopeSpec spec;
+  spec.kind = rope->kind;
+  spec.base = rope->base;
+  spec.factor = rope->factor;
+  spec.low_freq_factor = rope->low_freq_factor;
+  spec.high_freq_factor = rope->high_freq_factor;
+  spec.original_max_position = rope->original_max_position;
+  spec.theta = rope->theta;
+  const char* why = "";
+  if (!atw::rope_theta(spec, head_dim, theta, &why)) return fail(ATW_EINVAL, "rope: %s", why);
+  return ATW_OK;
+}
+
+atw_rope plain_rope(double base) {
+  atw_rope r{};
+  r.kind = ATW_ROPE_PLAIN;
+  r.base = base;
+  return r;
+}
+
+// Kernel view of the window from given frequencies: W_r clamped to INT32_MAX
+// and turns per position theta_r / (2*pi).
+void fill_window_theta(atw::WindowArgs* w, int head_dim, const double* theta, double k_turns, bool on) {
+  int64_t widths[atw::kMaxHeadDim / 2];
+  atw::window_widths_theta(head_dim / 2, theta, k_turns, on, widths);
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (int r = 0; r < atw::kMaxPairs; ++r) {
+    if (r < head_dim / 2) {
+      w->w[r] = widths[r] > (int64_t)atw::kWindowInf ? atw::kWindowInf : (int32_t)widths[r];
+      w->phi[r] = theta[r] / two_pi;
+    } else {
+      w->w[r] = atw::kWindowInf;
+      w->phi[r] = 0.0;
+    }
+  }
+}
+
 // Kernel view of the window: W_r clamped to INT32_MAX and turns per position.
 void fill_window(atw::WindowArgs* w, int head_dim, double rope_base, double k_turns, bool on) {
   int64_t widths[atw::kMaxHeadDim / 2];
@@ -126,6 +171,38 @@ int atw_pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim
   return ok();
 }
 
+int atw_rope_theta(const atw_rope* rope, int32_t head_dim, double* theta_out) {
+  if (theta_out == nullptr) return fail(ATW_EINVAL, "theta_out is NULL");
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, 1.0, 0, atw::kMaxHeadDim, theta)) return e;
+  for (int r = 0; r < head_dim / 2; ++r) theta_out[r] = theta[r];
+  return ok();
+}
+
+int atw_window_widths_rope(const atw_rope* rope, int32_t head_dim, double k_turns,
+                           int32_t window_on, int64_t* widths_out) {
+  if (widths_out == nullptr) return fail(ATW_EINVAL, "widths_out is NULL");
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, widths_out);
+  return ok();
+}
+
+int atw_pruned_terms_rope(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim,
+                          const atw_rope* rope, double k_turns, int32_t causal, int32_t window_on,
+                          int64_t* pruned, int64_t* total) {
+  if (pruned == nullptr || total == nullptr) return fail(ATW_EINVAL, "pruned/total is NULL");
+  if (n_q < 0 || n_kv < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "n_q, n_kv, q_pos0 must be >= 0");
+  if (n_q > (int64_t(1) << 40) || n_kv > (int64_t(1) << 40) || q_pos0 > (int64_t(1) << 40))
+    return fail(ATW_EINVAL, "sizes above 2^40 are not supported");
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  int64_t w[atw::kMaxHeadDim / 2];
+  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, w);
+  atw::pruned_terms(n_q, n_kv, q_pos0, head_dim, w, causal != 0, pruned, total);
+  return ok();
+}
+
 int atw_window_plan(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
                     int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t causal, int32_t tile_q,
                     int32_t tile_k, int32_t* plan_out) {
@@ -166,13 +243,16 @@ int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, i
   return hip_status(atw::launch_plan(p, (hipStream_t)stream), "plan kernel launch");
 }
 
-int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t batch,
-                int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q, int32_t h_kv,
-                const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
-                const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
-                double rope_base, double k_turns, int32_t causal, int32_t window_on,
-                double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t batch,
+                 int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q, int32_t h_kv,
+                 const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
+                 const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                 const double* theta, double k_turns, int32_t causal, int32_t window_on,
+                 double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "prefill supports head_dim 64 and 128 (got %d)", head_dim);
   if (dtype != ATW_F32 && dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "dtype must be ATW_F32 or ATW_BF16");
@@ -229,7 +309,7 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
       if (kvh[h] == kv) p.qh_of_kv[n++] = (int16_t)h;
   }
   p.kv_first[h_kv] = (int16_t)n;
-  fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
+  fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
   if (dtype == ATW_F32)
     return hip_status(atw::launch_prefill_f32(p, head_dim, (hipStream_t)stream), "prefill launch");
 
@@ -254,6 +334,39 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
   return hip_status(atw::launch_prefill_bf16(p, pk, head_dim, (hipStream_t)stream), "prefill launch");
 }
 
+}  // namespace
+
+extern "C" {
+
+int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype, int64_t batch,
+                int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q, int32_t h_kv,
+                const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
+                const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                double rope_base, double k_turns, int32_t causal, int32_t window_on,
+                double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  const atw_rope rope = plain_rope(rope_base);
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
+                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      softmax_scale, workspace, workspace_bytes, stream);
+}
+
+int atw_prefill_rope(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                     int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q,
+                     int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                     const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                     int32_t window_on, double softmax_scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
+                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      softmax_scale, workspace, workspace_bytes, stream);
+}
+
 size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,
                                    int32_t head_dim) {
   if (dtype != ATW_BF16 || batch <= 0 || h_kv <= 0 || n_kv <= 0 || head_dim <= 0) return 0;
@@ -272,10 +385,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
                 int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
                 int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
                 const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
-                const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
+                const int64_t* o_strides, const double* theta, double k_turns, int32_t causal,
                 int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
                 size_t workspace_bytes, void* stream, bool banded) {
-  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "decode supports head_dim 64 and 128 (got %d)", head_dim);
   if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 only");
@@ -347,7 +459,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   }
   p.kv_first[h_kv] = (int16_t)n;
   p.group = h_q / h_kv;
-  fill_window(&p.win, head_dim, rope_base, k_turns, window_on != 0);
+  fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
   return hip_status(atw::launch_decode(p, head_dim, banded, (hipStream_t)stream), "decode launch");
 }
 
@@ -360,8 +472,27 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
                int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
                size_t workspace_bytes, void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  const atw_rope rope = plain_rope(rope_base);
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
   return decode_impl(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, rope_base, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
+                     stream, false);
+}
+
+int atw_decode_rope(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                    int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                    int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                    const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                    const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                    int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return decode_impl(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, false);
 }
@@ -373,8 +504,29 @@ int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, v
                       const int64_t* v_strides, const int64_t* o_strides, double rope_base,
                       double k_turns, int32_t causal, int32_t window_on, double softmax_scale,
                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
+  const atw_rope rope = plain_rope(rope_base);
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
   return decode_impl(q, k_bands, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, rope_base, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
+                     stream, true);
+}
+
+int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cache, void* o,
+                           int32_t dtype, int64_t batch, const int64_t* kv_len,
+                           const int64_t* q_pos, int32_t h_q, int32_t h_kv,
+                           const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
+                           const int64_t* k_strides, const int64_t* v_strides,
+                           const int64_t* o_strides, const atw_rope* rope, double k_turns,
+                           int32_t causal, int32_t window_on, double softmax_scale,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return decode_impl(q, k_bands, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
 }

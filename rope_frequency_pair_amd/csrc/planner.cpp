@@ -4,6 +4,11 @@
 #include <algorithm>
 #include <cmath>
 
+// Every formula here is evaluated in IEEE double exactly as written (no fused
+// multiply-add contraction), so the integer windows match other IEEE double
+// evaluations of the same expressions bit for bit.
+#pragma STDC FP_CONTRACT OFF
+
 namespace atw {
 
 void window_widths(int head_dim, double rope_base, double k_turns, bool window_on, int64_t* w) {
@@ -26,6 +31,66 @@ void pair_turns_per_position(int head_dim, double rope_base, double* phi) {
   const int h = head_dim / 2;
   const double two_pi = 2.0 * 3.141592653589793;
   for (int r = 0; r < h; ++r) phi[r] = std::pow(rope_base, (-2.0 * r) / head_dim) / two_pi;
+}
+
+bool rope_theta(const RopeSpec& spec, int head_dim, double* theta, const char** why) {
+  const int h = head_dim / 2;
+  const double two_pi = 2.0 * 3.141592653589793;
+  auto bad = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (spec.kind == kRopeTable) {
+    if (spec.theta == nullptr) return bad("table frequencies are NULL");
+    for (int r = 0; r < h; ++r) theta[r] = spec.theta[r];
+  } else {
+    if (!(spec.base > 1.0) || std::isinf(spec.base)) return bad("rope base must be a finite value > 1");
+    for (int r = 0; r < h; ++r) theta[r] = std::pow(spec.base, (-2.0 * r) / head_dim);
+    if (spec.kind == kRopeLinear) {
+      if (!(spec.factor > 0.0) || std::isinf(spec.factor)) return bad("linear factor must be finite and > 0");
+      for (int r = 0; r < h; ++r) theta[r] = theta[r] / spec.factor;
+    } else if (spec.kind == kRopeLlama3) {
+      const double f = spec.factor, lo = spec.low_freq_factor, hi = spec.high_freq_factor;
+      const double L = spec.original_max_position;
+      if (!(f > 0.0) || std::isinf(f) || !(lo > 0.0) || !(hi > lo) || std::isinf(hi) ||
+          !(L > 0.0) || std::isinf(L))
+        return bad("llama3 scaling needs factor > 0, 0 < low_freq_factor < high_freq_factor, "
+                   "original_max_position > 0 (all finite)");
+      const double lo_wavelen = L / lo, hi_wavelen = L / hi;
+      for (int r = 0; r < h; ++r) {
+        const double t = theta[r];
+        const double wavelen = two_pi / t;
+        if (wavelen < hi_wavelen) {
+          theta[r] = t;
+        } else if (wavelen > lo_wavelen) {
+          theta[r] = t / f;
+        } else {
+          const double sm = (L / wavelen - lo) / (hi - lo);
+          theta[r] = (1.0 - sm) * t / f + sm * t;
+        }
+      }
+    } else if (spec.kind != kRopePlain) {
+      return bad("unknown rope kind");
+    }
+  }
+  for (int r = 0; r < h; ++r) {
+    if (!(theta[r] > 0.0) || std::isinf(theta[r])) return bad("every theta_r must be finite and > 0");
+    if (r > 0 && theta[r] > theta[r - 1]) return bad("theta_r must be non-increasing in r");
+  }
+  return true;
+}
+
+void window_widths_theta(int h, const double* theta, double k_turns, bool window_on, int64_t* w) {
+  if (!window_on || std::isinf(k_turns)) {
+    for (int r = 0; r < h; ++r) w[r] = kUnbounded;
+    return;
+  }
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (int r = 0; r < h; ++r) {
+    const double lam = two_pi / theta[r];
+    const double x = std::floor(k_turns * lam);
+    w[r] = (x >= 4611686018427387904.0) ? kUnbounded : static_cast<int64_t>(x);
+  }
 }
 
 int first_retained_pair(const int64_t* w, int h, int64_t delta) {

@@ -21,6 +21,35 @@ void window_widths(int head_dim, double rope_base, double k_turns, bool window_o
 // theta_r / (2*pi): turns per position of pair r.
 void pair_turns_per_position(int head_dim, double rope_base, double* phi);
 
+// RoPE frequencies of a model whose config rescales them ("Using the ports":
+// window tables are built from the RoPE base, the head dim and rope_scaling).
+enum RopeKind { kRopePlain = 0, kRopeLinear = 1, kRopeLlama3 = 2, kRopeTable = 3 };
+struct RopeSpec {
+  int kind = kRopePlain;
+  double base = 10000.0;
+  double factor = 1.0;                  // linear, llama3
+  double low_freq_factor = 1.0;         // llama3
+  double high_freq_factor = 4.0;        // llama3
+  double original_max_position = 8192;  // llama3
+  const double* theta = nullptr;        // table: theta_r for r < d/2
+};
+
+// theta_r of every pair (radians per position).  Plain: base^(-2r/d).
+// Linear: the plain frequencies divided by factor.  Llama3: pairs whose plain
+// wavelength is below original_max_position / high_freq_factor keep their
+// frequency, pairs whose wavelength is above original_max_position /
+// low_freq_factor are divided by factor, and in between the frequency is the
+// blend (1 - s) * theta / factor + s * theta with
+// s = (original_max_position / wavelength - low_freq_factor) /
+//     (high_freq_factor - low_freq_factor).  Table: as given.
+// Returns false, with a reason, unless every theta_r is finite, > 0 and
+// non-increasing in r (the windows then grow with r).
+bool rope_theta(const RopeSpec& spec, int head_dim, double* theta, const char** why);
+
+// W_r = floor(k * 2*pi / theta_r) from given frequencies (same operations as
+// window_widths, which it reproduces bit for bit for the plain frequencies).
+void window_widths_theta(int h, const double* theta, double k_turns, bool window_on, int64_t* w);
+
 // Number of pairs whose window is shorter than delta (pairs pruned at that
 // distance).  w is non-decreasing; h entries.
 int first_retained_pair(const int64_t* w, int h, int64_t delta);

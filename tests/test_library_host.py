@@ -187,3 +187,43 @@ def test_kcache_band_invalid_arguments(lib):
     assert band(rows=None) == atw.binding.ATW_EINVAL
     assert band(strides=binding._arr64([0, 0, 3])) == atw.binding.ATW_EUNSUPPORTED
     assert band(n=0, rows=None) == atw.binding.ATW_OK        # nothing to copy, nothing launched
+
+
+LLAMA32 = {"rope_type": "llama3", "factor": 32.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+           "original_max_position_embeddings": 8192}
+SCALINGS = [LLAMA32, dict(LLAMA32, factor=8.0), {"rope_type": "linear", "factor": 4.0},
+            {"rope_type": "linear", "factor": 1.0}]
+
+
+@pytest.mark.parametrize("sc", SCALINGS)
+def test_rope_scaling_widths_and_counts_bit_exact(lib, sc):
+    for d, base, k in ((128, 5e5, 8.0), (64, 1e6, 8.0), (128, 1e7, 64.0), (64, 1e4, 0.7)):
+        assert atw.window_widths(d, base, k, True, sc) == list(oracle.window_widths(d, base, k, True, sc))
+        theta = atw.rope_theta(d, base, sc)
+        assert np.allclose(theta, oracle.pair_frequencies(d, base, sc), rtol=4e-16, atol=0)
+        for n, q0 in ((1000, 0), (4097, 123), (131072, 0)):
+            assert atw.pruned_terms(n, n + q0, q0, d, base, k, True, True, sc) == \
+                oracle.pruned_terms(n, n + q0, q0, d, base, k, True, True, sc)
+
+
+def test_rope_table_and_plain_descriptor_match_plain(lib):
+    d, base = 128, 5e5
+    tab = {"rope_type": "table", "theta": atw.rope_theta(d, base)}
+    assert atw.window_widths(d, base, 8.0, True, tab) == atw.window_widths(d, base, 8.0, True)
+    assert atw.pruned_terms(5000, 5000, 0, d, None, 8.0, True, True, tab) == \
+        atw.pruned_terms(5000, 5000, 0, d, base, 8.0, True, True)
+
+
+@pytest.mark.parametrize("bad", [
+    {"rope_type": "table", "theta": [1.0, 0.5, 0.6, 0.1]},        # rising
+    {"rope_type": "table", "theta": [1.0, 0.5, 0.0, 0.0]},        # zero
+    {"rope_type": "table", "theta": [1.0, float("nan"), 0.1, 0.01]},
+    {"rope_type": "linear", "factor": 0.0},
+    {"rope_type": "linear", "factor": -2.0},
+    dict(LLAMA32, high_freq_factor=1.0),                          # high <= low
+    dict(LLAMA32, original_max_position_embeddings=0),
+])
+def test_rope_scaling_rejected(lib, bad):
+    with pytest.raises(atw.AtwError) as e:
+        atw.window_widths(8, 1e4, 1.0, True, bad)
+    assert e.value.code == binding.ATW_EINVAL

@@ -279,8 +279,8 @@ def test_planted_rotation_mistakes_are_caught(monkeypatch):
 def test_planted_boundary_mistake_is_caught(monkeypatch):
     real = window.window_widths
 
-    def exclusive(head_dim, rope_base, k_turns, window_on=True):   # keeps delta < W instead of <= W
-        w = real(head_dim, rope_base, k_turns, window_on)
+    def exclusive(head_dim, rope_base, k_turns, window_on=True, scaling=None):   # keeps delta < W, not <= W
+        w = real(head_dim, rope_base, k_turns, window_on, scaling)
         return np.where(w == window.UNBOUNDED, w, w - 1)
 
     monkeypatch.setattr(attention, "window_widths", exclusive)
