@@ -379,6 +379,36 @@ def main():
             "on_off_speedup": round(mb / ma, 3),
             "on_vs_row_layout_off": round(result["decode_512k"]["ms_off"] / ma, 3),
             "line_bytes_on": by_line}
+
+        # multi-token decode (draft tokens verified in one step) on the same
+        # banded cache: T tokens per sequence at positions L-T .. L-1
+        multi = {}
+        for T in (2, 4):
+            qm = torch.randn((wd.batch, T, wd.h_q, wd.head_dim), generator=synth.generator(wd.seed + T),
+                             device="cpu").to(torch.bfloat16).to(dev)
+            om = torch.empty_like(qm)
+            wsm = torch.empty(atw.decode_multi_workspace_bytes(wd.batch, T, wd.h_q, wd.head_dim, wd.splits),
+                              dtype=torch.uint8, device=dev)
+
+            def mstep(on, T=T, qm=qm, om=om, wsm=wsm):
+                atw.decode_multi(qm, kb, vc, [L] * wd.batch, [L - T] * wd.batch, rope_base=wd.rope_base,
+                                 k_turns=wd.k_turns, window_on=on, num_splits=wd.splits, k_banded=True,
+                                 workspace=wsm, out=om)
+
+            for _ in range(2):
+                mstep(True)
+                mstep(False)
+            a, b = [], []
+            for _ in range(6):
+                a += time_launches(lambda: mstep(True), stream, 1)
+                b += time_launches(lambda: mstep(False), stream, 1)
+            passes = -(-T // (16 // (wd.h_q // wd.h_kv)))
+            multi[str(T)] = {"ms_on": round(statistics.median(a), 4), "ms_off": round(statistics.median(b), 4),
+                             "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+                             "cache_passes": passes,
+                             "ms_per_token_on": round(statistics.median(a) / T, 4)}
+            del qm, om, wsm
+        result["decode_512k_multi_token_banded"] = multi
         del qd, kb, vc
         torch.cuda.empty_cache()
 

@@ -251,6 +251,39 @@ int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, v
                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * atw_decode_multi -- decode of q_len query tokens per sequence at
+ * consecutive positions q_pos[b], q_pos[b] + 1, ..., q_pos[b] + q_len - 1
+ * (the draft tokens that multi-token prediction or speculative decoding
+ * verifies in one step; "MiMo-V2.6-Pro-RL and MTP": the windows are used
+ * with MTP drafts), causal: token j of sequence b sees keys 0 ..
+ * q_pos[b] + j of its cache (the drafts' own keys appended before the call),
+ * with the window measured from its own position.  Token j's output equals
+ * that of atw_decode with q_pos = q_pos[b] + j and kv_len = q_pos[b] + j + 1.
+ *
+ *   q [batch, q_len, h_q, d]    q_strides[3] = element strides of (batch, head,
+ *                               token) (the token stride a multiple of 16 bytes)
+ *   o [batch, q_len, h_q, d]    o_strides[3] likewise
+ *   k_cache: row layout [batch, h_kv, L, d] (k_banded = 0) or the pair-banded
+ *   layout of atw_decode_banded (k_banded = 1); v_cache as for atw_decode;
+ *   kv_len[b] >= 1 with q_pos[b] + q_len - 1 >= kv_len[b] - 1.
+ *   workspace: atw_decode_multi_workspace_bytes(...) bytes.
+ *
+ * q_len 1..16; the (query head, token) pairs of one kv head form the columns of
+ * the score MFMA, so tokens are processed in groups of 16 / (query heads per
+ * kv head), one kernel pass over the caches per group.  RoPE frequencies from
+ * the descriptor (see atw_rope).  Other limits as for atw_decode.
+ */
+size_t atw_decode_multi_workspace_bytes(int64_t batch, int32_t q_len, int32_t h_q, int32_t head_dim,
+                                        int32_t num_splits);
+int atw_decode_multi(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                     int64_t batch, int32_t q_len, const int64_t* kv_len, const int64_t* q_pos,
+                     int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                     const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, int32_t k_banded, const atw_rope* rope,
+                     double k_turns, int32_t window_on, double softmax_scale, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * atw_kcache_band -- copy keys [t0, t0 + n_tokens) of a row-layout K cache
  * (k_rows [batch, h_kv, L, head_dim], row_strides = (batch, head, token)) into
  * a pair-banded one (k_bands as for atw_decode_banded, band_strides =

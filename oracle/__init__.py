@@ -51,4 +51,5 @@ from .attention import (  # noqa: F401
     windowed_scores,
     prefill,
     decode,
+    decode_multi,
 )

@@ -176,3 +176,37 @@ def decode(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal=True, 
                 q_hat = rope(q[b, hq][None, :], np.array([pos]), theta)[0]
                 out[bi, hi] = _row_output(q_hat, pos, k_hat, v64, k_pos, widths, scale, causal)
     return out
+
+
+def decode_multi(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, window_on=True, scale=None,
+                 kv_head_of_q=None, heads=None, batches=None, scaling=None):
+    """Windowed causal attention of q_len query tokens per sequence, float64.
+
+    q: [B, T, Hq, d] pre-RoPE; token j of batch b sits at position
+    q_pos[b] + j and attends, causally, to keys 0 .. q_pos[b] + j of the first
+    kv_len[b] keys (key j at position j), each token with the window measured
+    from its own position ("The idea": the window depends on the query-key
+    distance only).  Returns [len(batches), T, len(heads), d].
+    """
+    q = np.asarray(q)
+    bsz, n_tok, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    hmap = _head_map(h_q, h_kv, kv_head_of_q)
+    theta = pair_frequencies(d, rope_base, scaling)
+    widths = window_widths(d, rope_base, k_turns, window_on, scaling)
+    scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else scale
+    heads = list(range(h_q)) if heads is None else list(heads)
+    batches = list(range(bsz)) if batches is None else list(batches)
+    out = np.zeros((len(batches), n_tok, len(heads), d), dtype=np.float64)
+    for bi, b in enumerate(batches):
+        n_kv = int(kv_len[b])
+        k_pos = np.arange(n_kv, dtype=np.int64)
+        for hi, hq in enumerate(heads):
+            kvh = hmap[hq]
+            k_hat = rope(k_cache[b, kvh, :n_kv], k_pos, theta)
+            v64 = np.asarray(v_cache[b, kvh, :n_kv], dtype=np.float64)
+            for j in range(n_tok):
+                pos = int(q_pos[b]) + j
+                q_hat = rope(q[b, j, hq][None, :], np.array([pos]), theta)[0]
+                out[bi, j, hi] = _row_output(q_hat, pos, k_hat, v64, k_pos, widths, scale, True)
+    return out

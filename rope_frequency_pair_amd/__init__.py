@@ -19,6 +19,8 @@ from .binding import (  # noqa: F401
     AtwError,
     decode,
     decode_banded,
+    decode_multi,
+    decode_multi_workspace_bytes,
     kcache_band,
     decode_workspace_bytes,
     default_scale,

@@ -21,7 +21,8 @@ EXPORTED = [
     "atw_decode_workspace_bytes", "atw_pruned_terms",
     "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
     "atw_version", "atw_rope_theta", "atw_window_widths_rope", "atw_pruned_terms_rope",
-    "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope",
+    "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope", "atw_decode_multi",
+    "atw_decode_multi_workspace_bytes",
 ]
 
 ATW_ROPE_PLAIN, ATW_ROPE_LINEAR, ATW_ROPE_LLAMA3, ATW_ROPE_TABLE = 0, 1, 2, 3
@@ -129,6 +130,12 @@ def load_library(path=LIB_PATH):
     lib.atw_decode_rope.restype = ctypes.c_int
     lib.atw_decode_banded_rope.argtypes = lib.atw_decode_rope.argtypes
     lib.atw_decode_banded_rope.restype = ctypes.c_int
+    lib.atw_decode_multi.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _pi64, _pi64, _i32, _i32, _pi32,
+                                     _i32, _pi64, _pi64, _pi64, _pi64, _i32, _prope, _f64, _i32, _f64,
+                                     _i32, _vp, ctypes.c_size_t, _vp]
+    lib.atw_decode_multi.restype = ctypes.c_int
+    lib.atw_decode_multi_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
+    lib.atw_decode_multi_workspace_bytes.restype = ctypes.c_size_t
     lib.atw_last_error.argtypes = []
     lib.atw_last_error.restype = ctypes.c_char_p
     lib.atw_version.argtypes = []
@@ -356,6 +363,42 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
         float(scale or 0.0), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return out
+
+
+def decode_multi(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, window_on=True,
+                 scale=None, num_splits=64, kv_head_of_q=None, k_banded=False, workspace=None,
+                 out=None, stream=None, rope_scaling=None):
+    """Causal decode of q_len tokens per sequence at positions q_pos[b] ..
+    q_pos[b] + q_len - 1.  q [B, T, Hq, d] (T = q_len, any strides with d
+    contiguous); k_cache [B, Hkv, L, d] (or the banded layout when k_banded);
+    v_cache [B, Hkv, L, d].  Returns out [B, T, Hq, d]."""
+    import torch
+    lib = load_library()
+    B, T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=q.dtype, device=q.device)
+    need = lib.atw_decode_multi_workspace_bytes(B, T, Hq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
+    q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
+    rdesc = rope_descriptor(rope_base, rope_scaling)
+    qs = (q.stride(0), q.stride(2), q.stride(1))
+    os_ = (out.stride(0), out.stride(2), out.stride(1))
+    _check(lib.atw_decode_multi(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, T,
+        _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D, _arr64(qs),
+        _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]), _arr64(os_), int(bool(k_banded)),
+        ctypes.byref(rdesc), float(k_turns), int(window_on), float(scale or 0.0), int(num_splits),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream)))
+    return out
+
+
+def decode_multi_workspace_bytes(batch, q_len, h_q, head_dim, num_splits):
+    return load_library().atw_decode_multi_workspace_bytes(batch, q_len, h_q, head_dim, num_splits)
 
 
 def default_scale(head_dim):

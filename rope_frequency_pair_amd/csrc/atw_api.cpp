@@ -382,7 +382,8 @@ namespace {
 
 // Shared body of atw_decode (row-layout K cache) and atw_decode_banded.
 int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
-                int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                int64_t batch, int32_t q_len, int64_t q_tok_stride, int64_t o_tok_stride,
+                const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
                 int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
                 const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
                 const int64_t* o_strides, const double* theta, double k_turns, int32_t causal,
@@ -402,8 +403,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
       return fail(ATW_EINVAL, "kv_len[%lld] = %lld must be in 1..2^30", (long long)b, (long long)kv_len[b]);
     if (q_pos[b] < 0 || q_pos[b] >= (int64_t(1) << 30))
       return fail(ATW_EINVAL, "q_pos[%lld] out of range", (long long)b);
-    if (causal && q_pos[b] < kv_len[b] - 1)
-      return fail(ATW_EINVAL, "causal decode needs q_pos[%lld] >= kv_len - 1", (long long)b);
+    if (causal && q_pos[b] + q_len - 1 < kv_len[b] - 1)
+      return fail(ATW_EINVAL, "causal decode needs q_pos[%lld] + q_len - 1 >= kv_len - 1", (long long)b);
+    if (q_pos[b] + q_len - 1 >= (int64_t(1) << 30))
+      return fail(ATW_EINVAL, "q_pos[%lld] + q_len - 1 out of range", (long long)b);
   }
   int16_t kvh[atw::kMaxHeadsQ];
   if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
@@ -415,7 +418,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   if (int e = check_strides("v", v_strides, 3, 2)) return e;
   if (o_strides == nullptr || o_strides[0] < 0 || o_strides[1] < 0)
     return fail(ATW_EINVAL, "o_strides must be non-NULL and non-negative");
-  const size_t need = atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits);
+  const size_t need = (size_t)q_len * atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(ATW_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(ATW_EUNSUPPORTED, "workspace must be 16-byte aligned");
@@ -428,8 +431,11 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   p.ws = static_cast<float*>(workspace);
   p.qs[0] = q_strides[0];
   p.qs[1] = q_strides[1];
+  p.qs[2] = q_tok_stride;
   p.os[0] = o_strides[0];
   p.os[1] = o_strides[1];
+  p.os[2] = o_tok_stride;
+  p.q_len = q_len;
   for (int i = 0; i < 3; ++i) {
     p.ks[i] = k_strides[i];
     p.vs[i] = v_strides[i];
@@ -455,7 +461,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
         p.qh_of_kv[n++] = (int16_t)h;
         ++cnt;
       }
-    if (cnt > 16) return fail(ATW_EUNSUPPORTED, "decode supports at most 16 query heads per kv head");
+    if (cnt * q_len > 16)
+      return fail(ATW_EUNSUPPORTED, "decode supports at most 16 (query head, token) columns per kv head");
   }
   p.kv_first[h_kv] = (int16_t)n;
   p.group = h_q / h_kv;
@@ -476,7 +483,7 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   const atw_rope rope = plain_rope(rope_base);
   double theta[atw::kMaxHeadDim / 2];
   if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  return decode_impl(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+  return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
                      head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, false);
@@ -491,7 +498,7 @@ int atw_decode_rope(const void* q, const void* k_cache, const void* v_cache, voi
                     size_t workspace_bytes, void* stream) {
   double theta[atw::kMaxHeadDim / 2];
   if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  return decode_impl(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+  return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
                      head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, false);
@@ -508,7 +515,7 @@ int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, v
   const atw_rope rope = plain_rope(rope_base);
   double theta[atw::kMaxHeadDim / 2];
   if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  return decode_impl(q, k_bands, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+  return decode_impl(q, k_bands, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
                      head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
@@ -525,10 +532,74 @@ int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cac
                            void* stream) {
   double theta[atw::kMaxHeadDim / 2];
   if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  return decode_impl(q, k_bands, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+  return decode_impl(q, k_bands, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
                      head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
+}
+
+size_t atw_decode_multi_workspace_bytes(int64_t batch, int32_t q_len, int32_t h_q, int32_t head_dim,
+                                        int32_t num_splits) {
+  if (q_len <= 0) return 0;
+  return (size_t)q_len * atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits);
+}
+
+int atw_decode_multi(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                     int64_t batch, int32_t q_len, const int64_t* kv_len, const int64_t* q_pos,
+                     int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                     const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, int32_t k_banded, const atw_rope* rope,
+                     double k_turns, int32_t window_on, double softmax_scale, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  if (q_len < 1 || q_len > 16) return fail(ATW_EINVAL, "q_len must be in 1..16 (got %d)", q_len);
+  if (q_strides == nullptr || o_strides == nullptr) return fail(ATW_EINVAL, "q_strides / o_strides is NULL");
+  if (q_strides[2] < 0 || o_strides[2] < 0 || (q_strides[2] * 2) % 16 != 0)
+    return fail(ATW_EINVAL, "token strides must be non-negative (q: a multiple of 16 bytes)");
+  int16_t kvh[atw::kMaxHeadsQ];
+  if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
+  int gmax = 0;
+  for (int kv = 0; kv < h_kv; ++kv) {
+    int cnt = 0;
+    for (int h = 0; h < h_q; ++h) cnt += kvh[h] == kv;
+    gmax = cnt > gmax ? cnt : gmax;
+  }
+  if (gmax > 16) return fail(ATW_EUNSUPPORTED, "at most 16 query heads per kv head");
+  const size_t need = atw_decode_multi_workspace_bytes(batch, q_len, h_q, head_dim, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATW_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (batch <= 0 || batch > atw::kMaxDecodeBatch)
+    return fail(ATW_EUNSUPPORTED, "batch must be in 1..%d", atw::kMaxDecodeBatch);
+  if (kv_len == nullptr || q_pos == nullptr) return fail(ATW_EINVAL, "kv_len and q_pos must be non-NULL");
+  for (int64_t bb = 0; bb < batch; ++bb) {
+    if (kv_len[bb] < 1 || kv_len[bb] > (int64_t(1) << 30))
+      return fail(ATW_EINVAL, "kv_len[%lld] = %lld must be in 1..2^30", (long long)bb, (long long)kv_len[bb]);
+    if (q_pos[bb] < 0 || q_pos[bb] + q_len - 1 >= (int64_t(1) << 30))
+      return fail(ATW_EINVAL, "q_pos[%lld] out of range", (long long)bb);
+    if (q_pos[bb] + q_len - 1 < kv_len[bb] - 1)
+      return fail(ATW_EINVAL, "q_pos[%lld] + q_len - 1 >= kv_len - 1 is required", (long long)bb);
+  }
+  // the tokens go through the kernel in groups of at most 16 / gmax, one
+  // launch per group (each launch streams the caches once)
+  const int per = 16 / (gmax > 0 ? gmax : 1);
+  int64_t pos[atw::kMaxDecodeBatch], kvl[atw::kMaxDecodeBatch];
+  for (int t0 = 0; t0 < q_len; t0 += per) {
+    const int n = q_len - t0 < per ? q_len - t0 : per;
+    // the group's tokens see keys up to the position of its last token
+    for (int64_t bb = 0; bb < batch; ++bb) {
+      pos[bb] = q_pos[bb] + t0;
+      kvl[bb] = kv_len[bb] < pos[bb] + n ? kv_len[bb] : pos[bb] + n;
+    }
+    const void* qg = static_cast<const char*>(q) + (int64_t)t0 * q_strides[2] * 2;
+    void* og = static_cast<char*>(o) + (int64_t)t0 * o_strides[2] * 2;
+    if (int e = decode_impl(qg, k_cache, v_cache, og, dtype, batch, n, q_strides[2], o_strides[2], kvl,
+                            pos, h_q, h_kv, kv_head_of_q, head_dim, q_strides, k_strides, v_strides,
+                            o_strides, theta, k_turns, 1, window_on, softmax_scale, num_splits,
+                            workspace, workspace_bytes, stream, k_banded != 0))
+      return e;
+  }
+  return ok();
 }
 
 int atw_kcache_band(const void* k_rows, void* k_bands, int32_t dtype, int64_t batch, int32_t h_kv,

@@ -116,7 +116,16 @@ struct DSmem {
 // the token stride is 16.  A 128-byte line then holds one band of 4 keys,
 // so a band the window prunes for those keys is not fetched at all.
 // Otherwise K is [batch, h_kv, L, d] with ks[2] the token stride.
-template <int D, bool BANDED>
+// MULTI: q_len > 1 query tokens per sequence at consecutive positions q_pos,
+// q_pos + 1, ... (draft tokens of speculative / multi-token decoding), causal.
+// The MFMA columns are (token, query head) pairs, token-major.  K' is staged
+// with the window of token 0, the nearest one (distances grow with the token
+// index, so token 0 keeps the most pairs); a tile in which some key has a pair
+// whose window ends between the distances of token 0 and of the last token is
+// recomputed token by token from the rotated values kept in registers, each
+// lane keeping its own token's scores.  Keys after a token's position are
+// masked out of that token's column.
+template <int D, bool BANDED, bool MULTI>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(const DecodeParams p) {
   using C = DCfg<D>;
   constexpr int H = C::H;
@@ -137,12 +146,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const __bf16* vbase = (const __bf16*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
   // query operand (B of 16x16x32): column l16 = the l16-th query head of this
-  // kv head, contraction slots 8*grp4.. of k-step ks = pairs 16ks + 4grp4 + 0..3
+  // kv head (MULTI: token l16 / G, head l16 % G), contraction slots 8*grp4.. of
+  // k-step ks = pairs 16ks + 4grp4 + 0..3
+  const int q_len = MULTI ? p.q_len : 1;
+  const bool col_valid = l16 < G * q_len;
+  const int tok = (MULTI && col_valid) ? l16 / G : 0;
+  const int col_qh = col_valid ? p.qh_of_kv[g0 + (MULTI ? l16 % G : l16)] : 0;
   bf16x8 qop[C::NKS];
   {
-    const bool valid = l16 < G;
-    const int qh = valid ? p.qh_of_kv[g0 + l16] : 0;
-    const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + qh * p.qs[1];
+    const bool valid = col_valid;
+    const int qh = col_qh;
+    const int tpos = qpos + tok;
+    const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + qh * p.qs[1] + tok * p.qs[2];
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const int r0 = 16 * ks + 4 * grp4;
@@ -155,7 +170,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
           const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
           const float x2 = (u & 1) ? bf16_hi(c2[u >> 1]) : bf16_lo(c2[u >> 1]);
           float s, c;
-          rope_sincos(qpos, p.win.phi[r0 + u], &s, &c);
+          rope_sincos(tpos, p.win.phi[r0 + u], &s, &c);
           packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
         }
       }
@@ -228,8 +243,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   };
 
   int round_ix = 0;   // staging rounds done so far (drives the recurrence)
+  // MULTI: rotated, packed K' pairs of the staged tile (not yet windowed), and
+  // whether some key of the tile has a pair kept for token 0 but not for the
+  // last token
+  uint32_t rot[MULTI ? C::ROUNDS : 1][8];
+  bool nonuni = false;
   auto store_tile = [&](int t) {
     const int m0 = k_begin + t * kTK;
+    nonuni = false;
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
       const int m = m0 + C::KPR * i + kj;
@@ -245,6 +266,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
         const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
         uint32_t pk = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
+        if constexpr (MULTI) {
+          rot[i][e] = pk;
+          nonuni = nonuni || (dist <= wch[e] && dist + q_len - 1 > wch[e]);
+        }
         pk = dist > wch[e] ? 0u : pk;             // pair beyond its window at this key
         if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
       }
@@ -267,6 +292,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   };
 
+  // MULTI: rewrite the staged K' tile windowed for token j (distance + j)
+  auto rewrite_k = [&](int t, int j) {
+    const int m0 = k_begin + t * kTK;
+#pragma unroll
+    for (int i = 0; i < C::ROUNDS; ++i) {
+      const int m = m0 + C::KPR * i + kj;
+      const int dist = key_dist(m) + j;
+      u32x4 o0, o1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pk = dist > wch[e] ? 0u : rot[MULTI ? i : 0][e];
+        if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
+      }
+      __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
+      reinterpret_cast<u32x4*>(dst)[0] = o0;
+      reinterpret_cast<u32x4*>(dst)[1] = o1;
+    }
+  };
+
   if (n_tiles > 0) load_tile(0);
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -281,14 +325,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int r_any = wave_pairs_below(w_lane, dmin);   // pairs below: zero for every key
 
     // S^T = K' Q'^T over the k-steps that hold some kept pair
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    auto qk = [&](f32x4 (&s)[2]) {
+      s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      if (16 * ks + 16 <= r_any) continue;
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        if (16 * ks + 16 <= r_any) continue;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
-        sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[blk], 0, 0, 0);
+        for (int blk = 0; blk < 2; ++blk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[blk], 0, 0, 0);
+        }
+      }
+    };
+    f32x4 sacc[2];
+    qk(sacc);
+    if constexpr (MULTI) {
+      if (__any(nonuni)) {
+        // some pair's window ends between the tokens' distances in this tile:
+        // recompute for each later token from the rotated values
+        for (int j = 1; j < q_len; ++j) {
+          __syncthreads();
+          rewrite_k(t, j);
+          __syncthreads();
+          f32x4 sj[2];
+          qk(sj);
+          if (tok == j) {
+            sacc[0] = sj[0];
+            sacc[1] = sj[1];
+          }
+        }
+      }
+      // keys after a token's position (the later draft tokens' own keys)
+      if (m_hi > qpos) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (m_lo + 16 * blk + 4 * grp4 + v > qpos + tok) sacc[blk][v] = -INFINITY;
       }
     }
 
@@ -347,9 +421,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // partial result of this split: [m (raw score units), l, -, -, o[D]] per query head
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot = half_swap_sum(l_tot);
-  if (l16 < G) {
-    const int qh = p.qh_of_kv[g0 + l16];
-    float* w = p.ws + (((int64_t)b * p.h_q + qh) * p.splits + split) * (D + 4);
+  if (col_valid) {
+    const int qh = col_qh;
+    float* w = p.ws + ((((int64_t)b * q_len + tok) * p.h_q + qh) * p.splits + split) * (D + 4);
     if (grp4 == 0) {
       w[0] = m_run;
       w[1] = l_tot;
@@ -369,9 +443,11 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   constexpr int NW = D / 64;
   __shared__ float weight[kMaxDecodeSplits];
   __shared__ float part[NW];
-  const int qh = blockIdx.x, b = blockIdx.y, d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  // blockIdx.y = sequence * q_len + token
+  const int qh = blockIdx.x, bt = blockIdx.y, d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  const int b = bt / p.q_len, tok = bt % p.q_len;
   const int S = p.splits;
-  const float* w = p.ws + ((int64_t)b * p.h_q + qh) * S * (D + 4);
+  const float* w = p.ws + ((int64_t)bt * p.h_q + qh) * S * (D + 4);
   auto block_reduce = [&](float x, bool is_max) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -400,7 +476,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   float acc = 0.f;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) acc += weight[s] * w[s * (D + 4) + 4 + d];
-  __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1];
+  __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1] + tok * p.os[2];
   o[d] = (__bf16)(acc / l);
 }
 
@@ -425,18 +501,28 @@ __global__ __launch_bounds__(256) void kcache_band_kernel(const BandParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipStream_t stream) {
   dim3 grid((unsigned)p.splits, (unsigned)p.h_kv, (unsigned)p.batch);
-  dim3 cgrid((unsigned)p.h_q, (unsigned)p.batch);
+  dim3 cgrid((unsigned)p.h_q, (unsigned)(p.batch * p.q_len));
+  const bool multi = p.q_len > 1;
+#define ATW_DECODE_SPLIT(DD, BB, MM) \
+  hipLaunchKernelGGL((decode_split_kernel<DD, BB, MM>), grid, dim3(64), 0, stream, p)
   if (head_dim == 128) {
-    if (banded) hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(64), 0, stream, p);
+    if (multi) {
+      if (banded) ATW_DECODE_SPLIT(128, true, true); else ATW_DECODE_SPLIT(128, false, true);
+    } else {
+      if (banded) ATW_DECODE_SPLIT(128, true, false); else ATW_DECODE_SPLIT(128, false, false);
+    }
     hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(128), 0, stream, p);
   } else if (head_dim == 64) {
-    if (banded) hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(64), 0, stream, p);
+    if (multi) {
+      if (banded) ATW_DECODE_SPLIT(64, true, true); else ATW_DECODE_SPLIT(64, false, true);
+    } else {
+      if (banded) ATW_DECODE_SPLIT(64, true, false); else ATW_DECODE_SPLIT(64, false, false);
+    }
     hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(64), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
+#undef ATW_DECODE_SPLIT
   return hipGetLastError();
 }
 

@@ -42,10 +42,10 @@ struct DecodeParams {
   const void* k;
   const void* v;
   void* o;
-  float* ws;                             // [batch, h_q, splits, head_dim + 2]
-  int64_t qs[2], ks[3], vs[3], os[2];
+  float* ws;                             // [batch, q_len, h_q, splits, head_dim + 4]
+  int64_t qs[3], ks[3], vs[3], os[3];   // q / o: (batch, head, token) element strides
   int32_t batch, h_q, h_kv, splits;
-  int32_t causal, group, pad0, pad1;     // group = query heads per kv head
+  int32_t causal, group, q_len, pad1;   // group = query heads per kv head; q_len tokens per sequence
   float scale_log2;
   int32_t kv_len[kMaxDecodeBatch];
   int32_t q_pos[kMaxDecodeBatch];
