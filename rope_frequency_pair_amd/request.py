@@ -10,6 +10,16 @@ Host-side sequencing only: every computation is a libatw call.
 from . import binding
 
 
+def decode_splits(w):
+    """Split-KV count of the request's decode steps: the workload's own, else
+    enough (sequence, kv head, split) work items for ~8 per CU of the 256 CUs
+    (a single sequence with few kv heads would otherwise leave most CUs idle
+    and the step bound by memory latency rather than bandwidth)."""
+    if w.splits:
+        return w.splits
+    return max(64, -(-2048 // (w.batch * w.h_kv)))
+
+
 class RequestBuffers:
     """Device buffers a request needs beyond its inputs, allocated once."""
 
@@ -23,7 +33,7 @@ class RequestBuffers:
             binding.prefill_workspace_bytes(binding.ATW_BF16, w.batch, w.h_kv, w.n, w.head_dim),
             dtype=torch.uint8, device=device)
         self.ws_decode = torch.empty(
-            binding.decode_workspace_bytes(w.batch, w.h_q, w.head_dim, w.splits or 64),
+            binding.decode_workspace_bytes(w.batch, w.h_q, w.head_dim, decode_splits(w)),
             dtype=torch.uint8, device=device)
         self.k_bands = torch.empty((w.batch, w.h_kv, w.head_dim // 16, n_all, 16), dtype=w.dtype,
                                    device=device)
@@ -37,7 +47,7 @@ def run_request(w, q, q_dec, k, v, bufs, *, window_on=True, stream=None, on_chun
     keys [0, w.n + s].  Returns (out of the last prefill chunk, decode outputs
     [steps, B, Hq, d]); on_chunk(c, out) is called after each chunk."""
     n, ch = w.n, w.chunk
-    splits = w.splits or 64
+    splits = decode_splits(w)
     for c in range(n // ch):
         binding.prefill(q[:, :, c * ch:(c + 1) * ch], k[:, :, :(c + 1) * ch], v[:, :, :(c + 1) * ch],
                         rope_base=w.rope_base, k_turns=w.k_turns, q_pos0=c * ch, causal=True,
