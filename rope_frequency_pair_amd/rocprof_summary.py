@@ -110,7 +110,7 @@ def _print_counters(dbs):
                 print(f"| {_short(kn)} | {cn} | {len(vals)} | {statistics.mean(vals):.6g} |")
 
 
-def traffic(fetch_db, write_db, kernel, copy_bytes, copy_kernel="copy"):
+def traffic(fetch_db, write_db, kernel, copy_bytes, copy_kernel="copyBuffer"):
     def mean_for(db, counter, match):
         vals = []
         for kn, cs in counters(db).items():
@@ -149,7 +149,7 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
-    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--sha", default=None)
     t.add_argument("--out", default=None)
     a = ap.parse_args(argv)
