@@ -438,13 +438,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 // merge of (max, sum, unnormalised output) partials.  The splits' maxima and
 // weights are read by all threads at once (one split per thread, strided),
 // so the merge costs a few dependent memory round trips, not one per split.
+// The weighted sum of the outputs is spread over G = kCombineThreads / D
+// groups of D threads (group g takes splits g, g + G, ...), whose partial
+// sums meet in LDS: with hundreds of splits and a handful of blocks per
+// call (one sequence, few heads) a single group would walk the splits one
+// memory round trip after another.
+constexpr int kCombineThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p) {
-  constexpr int NW = D / 64;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams p) {
+  constexpr int T = kCombineThreads, NW = T / 64, G = T / D;
   __shared__ float weight[kMaxDecodeSplits];
   __shared__ float part[NW];
+  __shared__ float gsum[G - 1][D];
   // blockIdx.y = sequence * q_len + token
-  const int qh = blockIdx.x, bt = blockIdx.y, d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  const int qh = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int d = tid % D, g = tid / D;
   const int b = bt / p.q_len, tok = bt % p.q_len;
   const int S = p.splits;
   const float* w = p.ws + ((int64_t)bt * p.h_q + qh) * S * (D + 4);
@@ -463,10 +472,10 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
     return x;
   };
   float m = -INFINITY;
-  for (int s = d; s < S; s += D) m = fmaxf(m, w[s * (D + 4)]);
+  for (int s = tid; s < S; s += T) m = fmaxf(m, w[s * (D + 4)]);
   m = block_reduce(m, true);
   float l = 0.f;
-  for (int s = d; s < S; s += D) {
+  for (int s = tid; s < S; s += T) {
     const float ms = w[s * (D + 4)];
     const float a = (ms == -INFINITY) ? 0.f : exp2f((ms - m) * p.scale_log2);
     weight[s] = a;
@@ -475,9 +484,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   l = block_reduce(l, false);   // its barriers also publish weight[]
   float acc = 0.f;
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) acc += weight[s] * w[s * (D + 4) + 4 + d];
-  __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1] + tok * p.os[2];
-  o[d] = (__bf16)(acc / l);
+  for (int s = g; s < S; s += G) acc += weight[s] * w[s * (D + 4) + 4 + d];
+  if (g > 0) gsum[g - 1][d] = acc;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < G - 1; ++i) acc += gsum[i][d];
+    __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1] + tok * p.os[2];
+    o[d] = (__bf16)(acc / l);
+  }
 }
 
 // Row-layout K cache -> pair-banded K cache, for tokens [t0, t0 + n) of every
@@ -511,14 +526,14 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipSt
     } else {
       if (banded) ATW_DECODE_SPLIT(128, true, false); else ATW_DECODE_SPLIT(128, false, false);
     }
-    hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(kCombineThreads), 0, stream, p);
   } else if (head_dim == 64) {
     if (multi) {
       if (banded) ATW_DECODE_SPLIT(64, true, true); else ATW_DECODE_SPLIT(64, false, true);
     } else {
       if (banded) ATW_DECODE_SPLIT(64, true, false); else ATW_DECODE_SPLIT(64, false, false);
     }
-    hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(kCombineThreads), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
