@@ -21,9 +21,10 @@
 //  prefill_bf16_kernel -- one workgroup = 8 waves = 256 consecutive query
 //    rows of one query head; a wave owns 32 rows; key tiles of 64 keys,
 //    double-buffered in LDS:
-//  * staging is a plain copy of 1 KB blocks (wave w copies blocks w, w+8,
-//    ...); K' blocks of k-steps that the window prunes for the whole
-//    workgroup are neither loaded nor written;
+//  * staging copies 1 KB blocks straight from global memory into LDS
+//    (global_load_lds_dwordx4, no registers on the way; wave w copies blocks
+//    w, w+8, ...), one tile ahead; K' blocks of k-steps that the window
+//    prunes for the whole workgroup are not copied;
 //  * workgroups are dispatched largest causal blocks first, and the ones
 //    resident on one XCD (workgroup i runs on XCD i mod 8) are consecutive
 //    blocks of one (batch, kv head), so they share K'/V tiles in its L2;
@@ -34,17 +35,17 @@
 //  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
 //    k-step of 16 covers 8 whole pairs, so the retained pairs [r, h) are a
 //    contiguous range of k-steps;
-//  * pairs that are in the window for some cells of a wave's tile and not for
-//    others ("partial" pairs) are added first, one pair per MFMA, and after
-//    each such pair the cells beyond its window are reset to zero; because
-//    windows grow with r, this leaves exactly the kept partial terms; the
-//    fully kept pairs are added after;
+//  * per tile and wave: the k-step holding the first fully kept pair starts
+//    the accumulation (its partial slots masked out of the query operand),
+//    the fully kept k-steps above it follow; pairs that are in the window for
+//    some cells of the tile and not for others ("partial" pairs) go one pair
+//    per MFMA into a separate accumulator, and after each such pair the cells
+//    beyond its window are reset to zero; because windows grow with r, this
+//    leaves exactly the kept partial terms;
 //  * O^T += V^T P^T with P^T taken straight from the S^T registers (V is
 //    packed in the key order that register layout produces);
-//  * waves 0-3 run each tile as [QK^T, softmax, PV, staging of the next
-//    tile] and waves 4-7 as [staging, QK^T, softmax, PV], so on each SIMD
-//    the MFMA stretches of one wave meet the VALU stretches of the other;
-//    one workgroup barrier per tile;
+//  * one workgroup barrier per tile; tile geometry (distances, pair ranges)
+//    is wave-uniform and runs on the scalar unit;
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
 //  * head_dim 64 asks for four waves per SIMD (two workgroups per CU: 64 KB
@@ -270,15 +271,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
   const int kv_end = causal ? min(n_kv, gn_hi + 1) : n_kv;
   const int n_kt = (kv_end + kTK - 1) / kTK;
 
-  // ---- staging (global -> registers -> LDS), one tile ahead: while tile t
-  // is worked from LDS buffer t & 1, tile t+1 (loaded during tile t-1) is
-  // written to the other buffer and tile t+2 is loaded.  Wave w copies K'
-  // blocks w + 8i and V blocks w + 8i.  A K' block of a k-step that the window
-  // drops for every cell of the workgroup is not fetched: its load re-reads
-  // the wave's first V block of the tile (already on its way through the
-  // caches) and what lands in its LDS slot is never read.  Every load and
-  // write is unconditional, so no staging register is ever merged between
-  // paths.
+  // ---- staging: direct global -> LDS copies (global_load_lds_dwordx4: 16
+  // bytes per lane, lane l to byte 16 l of the destination, which is the
+  // operand-block layout itself), one tile ahead: while tile t is worked from
+  // LDS buffer t & 1, the copies of tile t+1 fill the other buffer and are
+  // waited for at the end of the tile, before the barrier.  No staging
+  // registers and no LDS store instructions.  Wave w copies K' blocks w + 8i
+  // and V blocks w + 8i; a K' block of a k-step that the window drops for
+  // every cell of the workgroup is not copied (its slot is never read).
   // First k-step any cell of the workgroup needs in key tile t (wave-uniform).
   auto stage_ks = [&](int t) -> int {
     const int m_lo = t * kTK;
@@ -287,41 +287,35 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
     if (!span32(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return C::NKS;
     return wave_pairs_below(w_lane, dmin) >> 3;
   };
-  u32x4 kreg[C::KPW], vreg[C::VPW];
-  auto load = [&](int t) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dma = [&](int t) {
     const int ks0 = stage_ks(t);
     const __bf16* ks = kpk + (int64_t)t * TILE;
     const __bf16* vs = vpk + (int64_t)t * TILE;
-#pragma unroll
-    for (int i = 0; i < C::VPW; ++i)
-      vreg[i] = *reinterpret_cast<const u32x4*>(vs + blk_off(wave + kWaves * i, lane));
-#pragma unroll
-    for (int i = 0; i < C::KPW; ++i) {
-      const int blk = wave + kWaves * i;
-      const __bf16* src = ((blk >> 1) >= ks0) ? ks + blk_off(blk, lane) : vs + blk_off(wave, lane);
-      kreg[i] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-  auto write = [&](int t) {
     __bf16* kd = &lk[t & 1][0];
     __bf16* vd = &lv[t & 1][0];
 #pragma unroll
-    for (int i = 0; i < C::KPW; ++i)
-      *reinterpret_cast<u32x4*>(kd + blk_off(wave + kWaves * i, lane)) = kreg[i];
+    for (int i = 0; i < C::VPW; ++i) {
+      const int blk = wave + kWaves * i;
+      __builtin_amdgcn_global_load_lds((const void*)(vs + blk_off(blk, lane)),
+                                       (lds_void*)(vd + blk_off(blk, 0)), 16, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < C::VPW; ++i)
-      *reinterpret_cast<u32x4*>(vd + blk_off(wave + kWaves * i, lane)) = vreg[i];
+    for (int i = 0; i < C::KPW; ++i) {
+      const int blk = wave + kWaves * i;
+      if ((blk >> 1) >= ks0)
+        __builtin_amdgcn_global_load_lds((const void*)(ks + blk_off(blk, lane)),
+                                         (lds_void*)(kd + blk_off(blk, 0)), 16, 0, 0);
+    }
   };
 
-  // ---- prologue: tile 0 in LDS, tile 1 in registers
-  load(0);
-  write(0);
-  if (n_kt > 1) load(1);
+  // ---- prologue: tile 0 in LDS
+  dma(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < n_kt; ++t) {
-    if (t + 1 < n_kt) write(t + 1);
-    if (t + 2 < n_kt) load(t + 2);
+    if (t + 1 < n_kt) dma(t + 1);
 
     const int m_lo = t * kTK;
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
@@ -486,6 +480,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       l_run += lsum;
     }
 
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t+1 have landed
     __syncthreads();
   }
 
