@@ -297,6 +297,52 @@ def main():
             "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
             "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
             "ceiling_2_over_1_plus_s": round(2.0 / (2.0 - sh), 3)}
+
+        # the window on top of a block-sparse token selection (64x64 blocks:
+        # the first key block, a local band of 4 blocks, and 10% of the earlier
+        # blocks drawn once per head for all its query blocks (vertical-slash
+        # shape) or independently per query block)
+        sparse = {}
+        for pattern, vertical in (("vertical_slash", True), ("independent_per_query_block", False)):
+            log(f"[bench] block-sparse selection at 128K: {pattern}")
+            sel = synth.block_selection(w.batch, w.h_q, w.n, w.n, w.seed + 100, vertical=vertical)
+            smask = atw.pack_block_mask(sel).to(q.device)
+            causal_blocks = (w.n // 64) * (w.n // 64 + 1) // 2 * w.h_q * w.batch
+            density = float(sel.sum()) / causal_blocks
+            del sel
+
+            def sstep(on):
+                atw.prefill_sparse(q, k, v, smask, rope_base=w.rope_base, k_turns=w.k_turns, window_on=on,
+                                   out=out)
+
+            sstep(True)
+            sstep(False)
+            a, b = [], []
+            for _ in range(6):
+                a += time_launches(lambda: sstep(True), stream, 1)
+                b += time_launches(lambda: sstep(False), stream, 1)
+            h = w.head_dim // 2
+            pr = tot = 0
+            for hq in range(w.h_q):
+                p_, t_ = atw.pruned_terms_sparse(w.n, w.n, 0, w.head_dim, w.rope_base, w.k_turns,
+                                                 smask[0, hq])
+                pr += p_
+                tot += t_
+            cells = tot // h
+            alg = (2 * w.head_dim * cells + 4 * (tot - pr)) * w.batch
+            dense_s = 4 * w.head_dim * cells * w.batch
+            sparse[pattern] = {
+                "block_density_of_causal": round(density, 4), "pruned_share": round(pr / tot, 4),
+                "ms_on": round(statistics.median(a), 3), "ms_off": round(statistics.median(b), 3),
+                "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+                "tflops_algorithmic_on": round(alg / (statistics.median(a) * 1e-3) / 1e12, 1),
+                "tflops_dense_equiv_on": round(dense_s / (statistics.median(a) * 1e-3) / 1e12, 1),
+                "ceiling_2_over_1_plus_s": round(2.0 / (2.0 - pr / tot), 3),
+                "speedup_vs_dense_window_on": round(med_on / statistics.median(a), 2)}
+            del smask
+        sparse["selection"] = ("64x64 blocks: first key block + local band of 4 + 10% of earlier blocks "
+                               "(vertical_slash: one draw per head; independent: one per query block)")
+        result["prefill_128k_block_sparse"] = sparse
         del q, k, v, out
         torch.cuda.empty_cache()
 

@@ -183,6 +183,55 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
                 double rope_base, double k_turns, int32_t causal, int32_t window_on,
                 double softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * atw_prefill_sparse -- atw_prefill composed with a block-sparse key
+ * selection: a token-level selection (as made by dynamic-sparse methods) is
+ * orthogonal to the frequency-level window, which therefore applies on top
+ * of it ("ATFlash: Per-RoPE-Wavelength Attention Windows for
+ * Compute/Memory-Efficient LLM Inference", arXiv abstract).
+ *
+ * Blocks are ATW_SPARSE_BLOCK = 64 query rows by 64 keys, counted from the
+ * start of the call's tensors (query block qb = rows [64 qb, 64 qb + 64) of
+ * q, key block kb = keys [64 kb, 64 kb + 64) of k).  A query attends key m
+ * iff the block of m is selected for the query's block, and (causal) m is
+ * not after the query's position; inside that set the per-pair window
+ * applies as in atw_prefill, and keys outside it are out of the softmax.  A
+ * query row that attends no key gets an output of 0.
+ *
+ *   block_mask: device uint32 [batch, h_q, ceil(n_q / 64), W] with
+ *     W = atw_block_mask_words(n_kv); bit kb % 32 of word kb / 32 of row
+ *     (b, hq, qb) set = query block qb of query head hq attends key block kb.
+ *     Bits for key blocks at or beyond ceil(n_kv / 64) are ignored.  Read
+ *     only, owned by the caller, 4-byte aligned.
+ *
+ * Every other argument, the workspace, the result codes and the limits as
+ * for atw_prefill_rope; dtype ATW_BF16 only (ATW_EUNSUPPORTED otherwise).
+ * With every bit of the mask set the output is bit-identical to atw_prefill.
+ */
+#define ATW_SPARSE_BLOCK 64
+int atw_prefill_sparse(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                       int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q,
+                       int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                       const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                       const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                       int32_t window_on, double softmax_scale, const uint32_t* block_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Words per block_mask row: ceil(ceil(n_kv / 64) / 32); 0 for n_kv <= 0. */
+int64_t atw_block_mask_words(int64_t n_kv);
+
+/*
+ * atw_pruned_terms_sparse -- host only.  atw_pruned_terms_rope over the cells
+ * a block-sparse selection attends, for one (batch, query head):
+ * block_mask is host uint32 [ceil(n_q / 64), atw_block_mask_words(n_kv)]
+ * (one head's rows of atw_prefill_sparse's mask).  Writes the pruned and
+ * total pair-terms of the attended cells (closed form per selected block
+ * and pair).
+ */
+int atw_pruned_terms_sparse(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim,
+                            const atw_rope* rope, double k_turns, int32_t causal, int32_t window_on,
+                            const uint32_t* block_mask, int64_t* pruned, int64_t* total);
+
 /* Workspace bytes atw_prefill needs: ATW_BF16: 2 * batch * h_kv *
  * ceil(n_kv / 64) * 64 * head_dim * 2 (one copy of K and V); ATW_F32: 0. */
 size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,

@@ -21,7 +21,8 @@ Modules:
 * :mod:`oracle.window`    -- per-pair frequencies, wavelengths, integer windows,
   the first retained pair at a distance, tile plans.
 * :mod:`oracle.counts`    -- pruned / total pair-term counts: brute force and
-  the per-row closed form; the large-N logarithmic approximation.
+  the per-row closed form; the large-N logarithmic approximation; the same
+  counts restricted to a block-sparse key selection.
 * :mod:`oracle.attention` -- RoPE, pair terms, windowed prefill and decode.
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
@@ -41,6 +42,8 @@ from .window import (  # noqa: F401
 )
 from .counts import (  # noqa: F401
     pruned_terms,
+    pruned_terms_blocks,
+    pruned_terms_blocks_bruteforce,
     pruned_terms_bruteforce,
     pruned_terms_square_closed_form,
     pruned_share_log_approx,

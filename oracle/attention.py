@@ -54,14 +54,17 @@ def pair_terms(q_hat, k_hat):
     return q_hat[None, :h] * k_hat[:, :h] + q_hat[None, h:] * k_hat[:, h:]
 
 
-def _row_output(q_hat, q_pos, k_hat, v, k_pos, widths, scale, causal):
-    """Output of one query row: windowed scores, softmax, weighted sum of v."""
+def _row_output(q_hat, q_pos, k_hat, v, k_pos, widths, scale, causal, allowed=None):
+    """Output of one query row: windowed scores, softmax, weighted sum of v.
+    allowed: optional boolean mask over the keys (a token-level selection);
+    keys outside it are out of the softmax, and a row attending no key is 0."""
     if causal:
         vis = k_pos <= q_pos
-        dist = q_pos - k_pos[vis]
     else:
         vis = np.ones(k_pos.shape, dtype=bool)
-        dist = np.abs(q_pos - k_pos)
+    if allowed is not None:
+        vis = vis & allowed
+    dist = np.abs(q_pos - k_pos[vis])
     if not vis.any():
         return np.zeros(v.shape[-1], dtype=np.float64)
     t = pair_terms(q_hat, k_hat[vis])
@@ -106,11 +109,19 @@ def _head_map(h_q, h_kv, kv_head_of_q):
 
 
 def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, scale=None,
-            kv_head_of_q=None, query_rows=None, heads=None, batches=None, scaling=None):
+            kv_head_of_q=None, query_rows=None, heads=None, batches=None, scaling=None,
+            key_blocks=None, block=64):
     """Windowed attention output for prefill, float64.
 
     q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nkv, d] (pre-RoPE).  Returns
     [len(batches), len(heads), len(query_rows), d] (defaults: all).
+
+    key_blocks: optional boolean block selection [B, Hq, ceil(Nq/block),
+    ceil(Nkv/block)]: query row i attends key j only if key_blocks[b, hq,
+    i // block, j // block] (a token-level selection, to which the window
+    applies on top: "ATFlash: Per-RoPE-Wavelength Attention Windows for
+    Compute/Memory-Efficient LLM Inference", arXiv abstract).  Rows attending
+    no key give 0.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -139,8 +150,11 @@ def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, sc
             q_pos = q_pos0 + rows
             q_hat = rope(q[b, hq, rows], q_pos, theta)
             for ri in range(len(rows)):
+                allowed = None
+                if key_blocks is not None:
+                    allowed = np.asarray(key_blocks[b, hq, int(rows[ri]) // block])[k_pos // block]
                 out[bi, hi, ri] = _row_output(q_hat[ri], int(q_pos[ri]), k_hat, v64, k_pos,
-                                              widths, scale, causal)
+                                              widths, scale, causal, allowed)
     return out
 
 

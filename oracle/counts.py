@@ -109,3 +109,58 @@ def pruned_share_log_approx(n, head_dim, rope_base, k_turns):
     of N, the logarithmic growth the pages state.
     """
     return (math.log(n / (2.0 * math.pi * k_turns)) - 1.5) / math.log(rope_base) + 1.0 / head_dim
+
+
+def pruned_terms_blocks(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, selected, causal=True,
+                        window_on=True, scaling=None, block=64):
+    """Exact (pruned, total) pair-term counts over the cells a block selection
+    attends (one head): selected[qb, kb] (boolean, ceil(n_q/block) x
+    ceil(n_kv/block)) lets query rows [qb*block, ...) see keys [kb*block, ...).
+    Per row and selected key block, the attended keys form one interval, and
+    pair r is pruned on the part of its distances above W_r (interval
+    counting in Python integers)."""
+    h = head_dim // 2
+    if n_q <= 0 or n_kv <= 0:
+        return 0, 0
+    widths = window_widths(head_dim, rope_base, k_turns, window_on, scaling)
+    selected = np.asarray(selected, dtype=bool)
+    pruned = 0
+    visible = 0
+    for i in range(n_q):
+        n = q_pos0 + i
+        for kb in np.nonzero(selected[i // block])[0]:
+            m0 = int(kb) * block
+            m1 = min(n_kv, m0 + block) - 1             # keys [m0, m1]
+            if causal:
+                m1 = min(m1, n)
+            if m1 < m0:
+                continue
+            visible += m1 - m0 + 1
+            for r in range(h):
+                w = int(widths[r])
+                # keys with n - m > w: m <= n - w - 1
+                pruned += max(0, min(m1, n - w - 1) - m0 + 1)
+                if not causal:
+                    # keys with m - n > w: m >= n + w + 1
+                    pruned += max(0, m1 - max(m0, n + w + 1) + 1)
+    return pruned, h * visible
+
+
+def pruned_terms_blocks_bruteforce(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, selected,
+                                   causal=True, window_on=True, scaling=None, block=64):
+    """Same counts by enumerating every attended (query, key, pair) triple
+    (small sizes only: materialises the cell grid)."""
+    h = head_dim // 2
+    if n_q <= 0 or n_kv <= 0:
+        return 0, 0
+    widths = window_widths(head_dim, rope_base, k_turns, window_on, scaling)
+    vis, dist = visible_cells(n_q, n_kv, q_pos0, causal)
+    sel = np.asarray(selected, dtype=bool)
+    qb = np.arange(n_q) // block
+    kb = np.arange(n_kv) // block
+    vis = vis & sel[qb[:, None], kb[None, :]]
+    d = dist[vis]
+    pruned = 0
+    for r in range(h):
+        pruned += int((d > widths[r]).sum())
+    return pruned, h * int(vis.sum())

@@ -14,20 +14,25 @@ from .binding import (  # noqa: F401
     ATW_BF16,
     ATW_F32,
     EXPORTED,
+    SPARSE_BLOCK,
     LIB_PATH,
     UNBOUNDED,
     AtwError,
+    block_mask_words,
     decode,
     decode_banded,
     decode_multi,
     decode_multi_workspace_bytes,
     kcache_band,
+    pack_block_mask,
     decode_workspace_bytes,
     default_scale,
     load_library,
     prefill,
+    prefill_sparse,
     prefill_workspace_bytes,
     pruned_terms,
+    pruned_terms_sparse,
     rope_descriptor,
     rope_theta,
     version,

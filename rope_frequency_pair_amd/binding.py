@@ -22,8 +22,11 @@ EXPORTED = [
     "atw_window_widths", "atw_window_plan", "atw_window_plan_device", "atw_last_error",
     "atw_version", "atw_rope_theta", "atw_window_widths_rope", "atw_pruned_terms_rope",
     "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope", "atw_decode_multi",
-    "atw_decode_multi_workspace_bytes",
+    "atw_decode_multi_workspace_bytes", "atw_prefill_sparse", "atw_block_mask_words",
+    "atw_pruned_terms_sparse",
 ]
+
+SPARSE_BLOCK = 64
 
 ATW_ROPE_PLAIN, ATW_ROPE_LINEAR, ATW_ROPE_LLAMA3, ATW_ROPE_TABLE = 0, 1, 2, 3
 
@@ -136,6 +139,13 @@ def load_library(path=LIB_PATH):
     lib.atw_decode_multi.restype = ctypes.c_int
     lib.atw_decode_multi_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
     lib.atw_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+    # prefill_rope's arguments with the block mask before the workspace
+    lib.atw_prefill_sparse.argtypes = lib.atw_prefill_rope.argtypes[:22] + [_vp] + lib.atw_prefill_rope.argtypes[22:]
+    lib.atw_prefill_sparse.restype = ctypes.c_int
+    lib.atw_block_mask_words.argtypes = [_i64]
+    lib.atw_block_mask_words.restype = ctypes.c_int64
+    lib.atw_pruned_terms_sparse.argtypes = [_i64, _i64, _i64, _i32, _prope, _f64, _i32, _i32, _vp, _pi64, _pi64]
+    lib.atw_pruned_terms_sparse.restype = ctypes.c_int
     lib.atw_last_error.argtypes = []
     lib.atw_last_error.restype = ctypes.c_char_p
     lib.atw_version.argtypes = []
@@ -220,6 +230,45 @@ def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, w
     return p.value, t.value
 
 
+def block_mask_words(n_kv):
+    """uint32 words per block-mask row: ceil(ceil(n_kv / 64) / 32)."""
+    return load_library().atw_block_mask_words(int(n_kv))
+
+
+def pack_block_mask(selected):
+    """Bit-pack a boolean block selection [..., n_qb, n_kb] (query block qb
+    attends key block kb) into the int32 words atw_prefill_sparse reads
+    [..., n_qb, ceil(n_kb / 32)] (bit kb % 32 of word kb / 32).  Host-side
+    marshalling of a torch bool tensor; the result is on the same device."""
+    import torch
+    n_kb = selected.shape[-1]
+    words = -(-n_kb // 32)
+    pad = words * 32 - n_kb
+    sel = torch.nn.functional.pad(selected.to(torch.int64), (0, pad))
+    sel = sel.reshape(*selected.shape[:-1], words, 32)
+    weights = torch.ones(32, dtype=torch.int64, device=selected.device) << torch.arange(32, device=selected.device)
+    packed = (sel * weights).sum(-1)
+    return torch.where(packed >= 2 ** 31, packed - 2 ** 32, packed).to(torch.int32).contiguous()
+
+
+def pruned_terms_sparse(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, block_mask, causal=True,
+                        window_on=True, rope_scaling=None):
+    """(pruned, total) pair-term counts over the cells one head's block-sparse
+    selection attends; block_mask: packed int32 words [ceil(n_q/64), words]
+    (any device; copied to the host)."""
+    import numpy as np
+    lib = load_library()
+    m = np.ascontiguousarray(block_mask.cpu().numpy().astype(np.int32).view(np.uint32))
+    if m.shape != (-(-n_q // SPARSE_BLOCK), block_mask_words(n_kv)):
+        raise ValueError("block_mask must be [ceil(n_q/64), block_mask_words(n_kv)]")
+    r = rope_descriptor(rope_base, rope_scaling)
+    p, t = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.atw_pruned_terms_sparse(n_q, n_kv, q_pos0, head_dim, ctypes.byref(r), float(k_turns),
+                                       int(causal), int(window_on), m.ctypes.data_as(ctypes.c_void_p),
+                                       ctypes.byref(p), ctypes.byref(t)))
+    return p.value, t.value
+
+
 def window_plan(head_dim, rope_base, k_turns, window_on, n_q, n_kv, q_pos0, causal, tile_q, tile_k):
     """Host tile plan as a nested list [n_qt][n_kt] of (r_any, r_full)."""
     lib = load_library()
@@ -284,6 +333,41 @@ def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=Tru
         _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
         _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), rope_arg, float(k_turns),
         int(causal), int(window_on), float(scale or 0.0), ws_ptr, ws_len, _stream_ptr(stream)))
+    return out
+
+
+def prefill_sparse(q, k, v, block_mask, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=True,
+                   scale=None, kv_head_of_q=None, out=None, workspace=None, stream=None,
+                   rope_scaling=None):
+    """prefill() restricted to a block-sparse key selection: block_mask is the
+    packed int32 device tensor [B, Hq, ceil(Nq/64), block_mask_words(Nkv)]
+    (pack_block_mask).  bf16 only."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise AtwError(ATW_EINVAL, f"{name} must be 4-D with a contiguous last dim")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    want = (B, Hq, -(-Nq // SPARSE_BLOCK), block_mask_words(Nkv))
+    if (block_mask.dtype != torch.int32 or tuple(block_mask.shape) != want or not block_mask.is_contiguous()
+            or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be a contiguous int32 tensor {want} on {q.device}")
+    need = lib.atw_prefill_workspace_bytes(_dtype_code(q), B, Hkv, Nkv, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rdesc = rope_descriptor(rope_base, rope_scaling)
+    _check(lib.atw_prefill_sparse(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
+        _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
+        _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), ctypes.byref(rdesc), float(k_turns),
+        int(causal), int(window_on), float(scale or 0.0), ctypes.c_void_p(block_mask.data_ptr()),
+        ws_ptr, ws_len, _stream_ptr(stream)))
     return out
 
 

@@ -252,9 +252,15 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
                  const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
                  const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
                  const double* theta, double k_turns, int32_t causal, int32_t window_on,
-                 double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                 double softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                 const uint32_t* block_mask = nullptr, bool sparse = false) {
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "prefill supports head_dim 64 and 128 (got %d)", head_dim);
+  if (sparse) {
+    if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "block-sparse prefill supports dtype ATW_BF16 only");
+    if (block_mask == nullptr && n_q > 0) return fail(ATW_EINVAL, "block_mask is NULL");
+    if (reinterpret_cast<uintptr_t>(block_mask) % 4 != 0) return fail(ATW_EINVAL, "block_mask must be 4-byte aligned");
+  }
   if (dtype != ATW_F32 && dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "dtype must be ATW_F32 or ATW_BF16");
   if (batch <= 0 || n_q < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "batch > 0, n_q >= 0, q_pos0 >= 0 required");
   if (n_kv < 1) return fail(ATW_EINVAL, "n_kv must be >= 1");
@@ -310,6 +316,11 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   }
   p.kv_first[h_kv] = (int16_t)n;
   fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
+  if (sparse) {
+    p.sel = block_mask;
+    p.n_sel_qb = (int32_t)((n_q + atw::kSparseBlock - 1) / atw::kSparseBlock);
+    p.sel_words = (int32_t)atw_block_mask_words(n_kv);
+  }
   if (dtype == ATW_F32)
     return hip_status(atw::launch_prefill_f32(p, head_dim, (hipStream_t)stream), "prefill launch");
 
@@ -365,6 +376,48 @@ int atw_prefill_rope(const void* q, const void* k, const void* v, void* o, int32
   return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
                       q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
                       softmax_scale, workspace, workspace_bytes, stream);
+}
+
+int atw_prefill_sparse(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                       int64_t batch, int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q,
+                       int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                       const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                       const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                       int32_t window_on, double softmax_scale, const uint32_t* block_mask,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
+                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      softmax_scale, workspace, workspace_bytes, stream, block_mask, true);
+}
+
+int64_t atw_block_mask_words(int64_t n_kv) {
+  if (n_kv <= 0) return 0;
+  const int64_t n_kb = (n_kv + atw::kSparseBlock - 1) / atw::kSparseBlock;
+  return (n_kb + 31) / 32;
+}
+
+int atw_pruned_terms_sparse(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim,
+                            const atw_rope* rope, double k_turns, int32_t causal, int32_t window_on,
+                            const uint32_t* block_mask, int64_t* pruned, int64_t* total) {
+  if (pruned == nullptr || total == nullptr) return fail(ATW_EINVAL, "pruned/total is NULL");
+  if (n_q < 0 || n_kv < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "n_q, n_kv, q_pos0 must be >= 0");
+  if (n_q > (int64_t(1) << 40) || n_kv > (int64_t(1) << 40) || q_pos0 > (int64_t(1) << 40))
+    return fail(ATW_EINVAL, "sizes above 2^40 are not supported");
+  if (block_mask == nullptr && n_q > 0 && n_kv > 0) return fail(ATW_EINVAL, "block_mask is NULL");
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  int64_t w[atw::kMaxHeadDim / 2];
+  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, w);
+  if (n_q == 0 || n_kv == 0) {
+    *pruned = 0;
+    *total = 0;
+    return ok();
+  }
+  atw::pruned_terms_blocks(n_q, n_kv, q_pos0, head_dim, w, causal != 0, block_mask,
+                           atw_block_mask_words(n_kv), atw::kSparseBlock, pruned, total);
+  return ok();
 }
 
 size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,

@@ -28,6 +28,11 @@ struct PrefillParams {
   int32_t h_q, causal, n_qblk, n_kv_heads;
   int32_t n_kt;                          // packed key tiles per (batch, kv head)
   float scale_log2;                      // softmax scale * log2(e)
+  // Block-sparse key selection (nullptr: every key).  Bit kb % 32 of word
+  // kb / 32 of row ((b * h_q + hq) * n_sel_qb + qb), rows of sel_words words:
+  // query block qb (64 rows) attends key block kb (64 keys).
+  const uint32_t* sel;
+  int32_t sel_words, n_sel_qb;
   int16_t qh_of_kv[kMaxHeadsQ];          // query heads grouped by kv head (kv-major)
   int16_t kv_first[kMaxHeadsQ + 1];      // start of each kv head's group in qh_of_kv
   WindowArgs win;
@@ -35,6 +40,7 @@ struct PrefillParams {
 
 // Decode: split-KV over the key axis, then a combine pass.
 constexpr int kDecodeTileK = 64;
+constexpr int kSparseBlock = 64;         // query rows / keys per block of a block-sparse selection
 constexpr int kMaxDecodeSplits = 1024;
 
 struct DecodeParams {

@@ -129,6 +129,24 @@ i128 noncausal_after_rows(i128 A, i128 B, i128 W, i128 n_kv) {
   return series(K - hi + 1, K - A + 1);
 }
 
+// sum_{x=lo}^{hi-1} clamp(x, 0, L)
+i128 sum_clamp(i128 lo, i128 hi, i128 L) {
+  if (hi <= lo || L <= 0) return 0;
+  i128 s = series(std::max<i128>(lo, 1), std::min<i128>(hi, L + 1));
+  const i128 full_lo = std::max<i128>(lo, L + 1);
+  if (hi > full_lo) s += (hi - full_lo) * L;
+  return s;
+}
+
+// Cells (n, m) of the rectangle rows [A, B) x keys [m0, m1) (positions) with
+// n - m > W, and with m - n > W.
+i128 rect_before(i128 A, i128 B, i128 m0, i128 m1, i128 W) {
+  return sum_clamp(A - W - m0, B - W - m0, m1 - m0);   // #{m in [m0, m1): m < n - W}
+}
+i128 rect_after(i128 A, i128 B, i128 m0, i128 m1, i128 W) {
+  return sum_clamp(m1 - W - B, m1 - W - A, m1 - m0);   // #{m in [m0, m1): m > n + W}
+}
+
 }  // namespace
 
 void pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
@@ -190,6 +208,33 @@ void tile_plan(int head_dim, const int64_t* w, int64_t n_q, int64_t n_kv, int64_
       out[1] = first_retained_pair(w, h, dmax);
     }
   }
+}
+
+void pruned_terms_blocks(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
+                         bool causal, const uint32_t* mask, int64_t mask_words, int block,
+                         int64_t* pruned, int64_t* total) {
+  const int h = head_dim / 2;
+  const int64_t n_qb = (n_q + block - 1) / block, n_kb = (n_kv + block - 1) / block;
+  i128 p = 0, visible = 0;
+  for (int64_t qb = 0; qb < n_qb; ++qb) {
+    const i128 A = (i128)q_pos0 + qb * block, B = (i128)q_pos0 + std::min<int64_t>(n_q, (qb + 1) * block);
+    const uint32_t* row = mask + qb * mask_words;
+    for (int64_t kb = 0; kb < n_kb; ++kb) {
+      if (!((row[kb >> 5] >> (kb & 31)) & 1u)) continue;
+      const i128 m0 = kb * block, m1 = std::min<int64_t>(n_kv, (kb + 1) * block);
+      if (causal) {
+        const i128 vis = rect_before(A, B, m0, m1, -1);   // m <= n
+        if (vis == 0) continue;
+        visible += vis;
+        for (int r = 0; r < h; ++r) p += rect_before(A, B, m0, m1, w[r]);
+      } else {
+        visible += (B - A) * (m1 - m0);
+        for (int r = 0; r < h; ++r) p += rect_before(A, B, m0, m1, w[r]) + rect_after(A, B, m0, m1, w[r]);
+      }
+    }
+  }
+  *pruned = static_cast<int64_t>(p);
+  *total = static_cast<int64_t>(visible * h);
 }
 
 }  // namespace atw

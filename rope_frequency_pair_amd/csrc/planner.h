@@ -60,6 +60,14 @@ int first_retained_pair(const int64_t* w, int h, int64_t delta);
 void pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
                   bool causal, int64_t* pruned, int64_t* total);
 
+// pruned_terms restricted to a block-sparse key selection: query block qb
+// (rows [qb * block, ...)) attends key block kb (keys [kb * block, ...)) iff
+// bit kb % 32 of mask[qb * mask_words + kb / 32] is set.  Closed form per
+// selected rectangle and pair.
+void pruned_terms_blocks(int64_t n_q, int64_t n_kv, int64_t q_pos0, int head_dim, const int64_t* w,
+                         bool causal, const uint32_t* mask, int64_t mask_words, int block,
+                         int64_t* pruned, int64_t* total);
+
 // Smallest and largest distance over the visible cells of the tile
 // rows [n_lo, n_hi] x keys [m_lo, m_hi] (positions).  Returns false when the
 // tile has no visible cell.

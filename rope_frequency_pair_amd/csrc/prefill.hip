@@ -174,7 +174,7 @@ __device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, b
   return true;
 }
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel(const PrefillParams p) {
   using C = PCfg<D>;
   constexpr int H = C::H;
@@ -273,9 +273,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
 
   // ---- staging: direct global -> LDS copies (global_load_lds_dwordx4: 16
   // bytes per lane, lane l to byte 16 l of the destination, which is the
-  // operand-block layout itself), one tile ahead: while tile t is worked from
-  // LDS buffer t & 1, the copies of tile t+1 fill the other buffer and are
-  // waited for at the end of the tile, before the barrier.  No staging
+  // operand-block layout itself), one tile ahead: while a tile is worked from
+  // one LDS buffer, the copies of the next visited tile fill the other and
+  // are waited for at the end of the tile, before the barrier.  No staging
   // registers and no LDS store instructions.  Wave w copies K' blocks w + 8i
   // and V blocks w + 8i; a K' block of a k-step that the window drops for
   // every cell of the workgroup is not copied (its slot is never read).
@@ -288,12 +288,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
     return wave_pairs_below(w_lane, dmin) >> 3;
   };
   typedef __attribute__((address_space(3))) void lds_void;
-  auto dma = [&](int t) {
+  auto dma = [&](int t, int slot) {
     const int ks0 = stage_ks(t);
     const __bf16* ks = kpk + (int64_t)t * TILE;
     const __bf16* vs = vpk + (int64_t)t * TILE;
-    __bf16* kd = &lk[t & 1][0];
-    __bf16* vd = &lv[t & 1][0];
+    __bf16* kd = &lk[slot][0];
+    __bf16* vd = &lv[slot][0];
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const int blk = wave + kWaves * i;
@@ -309,23 +309,74 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
     }
   };
 
-  // ---- prologue: tile 0 in LDS
-  dma(0);
+  // ---- key tiles visited, ascending.  Dense: 0 .. n_kt-1.  Block-sparse
+  // (composition with a token-level selection): the tiles that some 64-row
+  // query block of this workgroup selected, read 32 at a time from the
+  // selection words (scalar loads, wave-uniform); a wave works a tile only
+  // when its own query block selected it, and copies it to LDS either way.
+  int cursor = -1;                 // dense: last tile handed out
+  int sel_w = -1;                  // sparse: mask word being consumed
+  uint32_t sel_rest = 0;           // sparse: union bits of word sel_w not yet handed out
+  uint32_t sel_own = 0;            // sparse: this wave's bits of word sel_w
+  const uint32_t* sel_row0 = nullptr;
+  int n_sel_blk = 0, own_blk = 0;
+  const int n_words = (n_kt + 31) >> 5;
+  if constexpr (SPARSE) {
+    const int qb0 = i0 / kSparseBlock;
+    sel_row0 = p.sel + ((int64_t)(bb * p.h_q + hq) * p.n_sel_qb + qb0) * p.sel_words;
+    n_sel_blk = min(kPrefillBlockRows / kSparseBlock, p.n_sel_qb - qb0);
+    own_blk = (wave * kRowsW) / kSparseBlock;
+  }
+  auto next_tile = [&](int* t, bool* own) {
+    if constexpr (!SPARSE) {
+      ++cursor;
+      *t = cursor < n_kt ? cursor : -1;
+      *own = true;
+    } else {
+      while (sel_rest == 0) {
+        if (++sel_w >= n_words) {
+          *t = -1;
+          *own = false;
+          return;
+        }
+        const uint32_t valid = (n_kt - 32 * sel_w >= 32) ? 0xffffffffu : ((1u << (n_kt - 32 * sel_w)) - 1u);
+        uint32_t u = 0, mine = 0;
+        for (int j = 0; j < n_sel_blk; ++j) {
+          const uint32_t word = __builtin_amdgcn_readfirstlane(sel_row0[(int64_t)j * p.sel_words + sel_w]);
+          u |= word;
+          if (j == own_blk) mine = word;
+        }
+        sel_rest = u & valid;
+        sel_own = mine;
+      }
+      const int b = __builtin_ctz(sel_rest);
+      sel_rest &= sel_rest - 1;
+      *t = 32 * sel_w + b;
+      *own = ((sel_own >> b) & 1u) != 0;
+    }
+  };
+
+  // ---- prologue: the first tile in LDS
+  int t = -1, t_next = -1, slot = 0;
+  bool own = false, own_next = false;
+  next_tile(&t, &own);
+  if (t >= 0) dma(t, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < n_kt; ++t) {
-    if (t + 1 < n_kt) dma(t + 1);
+  while (t >= 0) {
+    next_tile(&t_next, &own_next);
+    if (t_next >= 0) dma(t_next, slot ^ 1);
 
     const int m_lo = t * kTK;
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
     int dmin = 0, dmax = 0;
-    if (wave_rows && span32(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
+    if (own && wave_rows && span32(n_lo, n_hi, m_lo, m_hi, causal, &dmin, &dmax)) {
       const int r_any = wave_pairs_below(w_lane, dmin);
       const int r_full = wave_pairs_below(w_lane, dmax);
       const int kbase_lane = m_lo + 4 * sh;
-      const __bf16* kt = &lk[t & 1][0];
-      const __bf16* vt = &lv[t & 1][0];
+      const __bf16* kt = &lk[slot][0];
+      const __bf16* vt = &lv[slot][0];
       f32x16 sacc[2];
 
       // reset the cells of x beyond the window of partially windowed pair pp
@@ -480,13 +531,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       l_run += lsum;
     }
 
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t+1 have landed
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
+    t = t_next;
+    own = own_next;
+    slot ^= 1;
   }
 
   // ---- epilogue: O = O^T / l
   const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // a row without an attended key gives 0
   const int row = w_first + l32;
   if (wave_rows && row <= w_last) {
     __bf16* orow = obase + (int64_t)row * p.os[2];
@@ -513,10 +567,16 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int
   dim3 grid((unsigned)blocks), block(kThreads);
   if (head_dim == 128) {
     hipLaunchKernelGGL(pack_kv_kernel<128>, pgrid, dim3(256), 0, stream, pk);
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, p);
+    if (p.sel)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p);
   } else if (head_dim == 64) {
     hipLaunchKernelGGL(pack_kv_kernel<64>, pgrid, dim3(256), 0, stream, pk);
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, p);
+    if (p.sel)
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

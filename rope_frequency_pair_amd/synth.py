@@ -111,3 +111,31 @@ def request_inputs(w, device="cuda"):
     for h in range(w.h_kv):
         v[:, h] = _randn((w.batch, n_all, w.head_dim), g, device, w.dtype)
     return q, q_dec, k, v
+
+
+def block_selection(batch, h_q, n_q, n_kv, seed, density=0.1, sink=1, local=4, block=64, q_pos0=0,
+                    vertical=False):
+    """Seeded boolean block selection [batch, h_q, ceil(n_q/block),
+    ceil(n_kv/block)] with the structure block-sparse attention methods
+    produce: the first `sink` key blocks, a local band of `local` key blocks
+    ending at the block holding the query block's last position, and earlier
+    key blocks with probability `density`: drawn independently per (batch,
+    head, query block), or with vertical=True once per (batch, head) and
+    shared by all its query blocks (vertical lines plus the diagonal band, the
+    vertical-slash shape).  Blocks after the band stay unselected.  Drawn with
+    numpy's PCG64 generator seeded with `seed` on the host."""
+    import numpy as np
+    n_qb, n_kb = -(-n_q // block), -(-n_kv // block)
+    rng = np.random.default_rng(seed)
+    if vertical:
+        sel = np.broadcast_to(rng.random((batch, h_q, 1, n_kb), dtype=np.float32) < density,
+                              (batch, h_q, n_qb, n_kb)).copy()
+    else:
+        sel = rng.random((batch, h_q, n_qb, n_kb), dtype=np.float32) < density
+    kb = np.arange(n_kb)[None, :]
+    last_pos = q_pos0 + np.minimum((np.arange(n_qb) + 1) * block, n_q) - 1
+    diag = np.minimum(last_pos // block, n_kb - 1)[:, None]
+    sel &= (kb <= diag)[None, None]
+    band = (kb <= diag) & (kb > diag - local)
+    sel |= (band | (kb < sink))[None, None]
+    return torch.from_numpy(sel)

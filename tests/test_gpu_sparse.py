@@ -1,0 +1,119 @@
+"""GPU parity of the block-sparse composition (atw_prefill_sparse): a
+token-level block selection decides which keys a query attends and the
+per-pair window applies on top of it ("ATFlash: Per-RoPE-Wavelength Attention
+Windows for Compute/Memory-Efficient LLM Inference", arXiv abstract).  Checked
+against the fp64 oracle with the same selection: whole outputs at sizes with
+several workgroups, key tiles and a ragged tail, query blocks that attend
+nothing, a chunk (q_pos0 > 0), non-causal, rescaled frequencies, and sampled
+rows at the 128K Llama-3.2-3B shape; and bit-identity with the dense path
+when every block is selected."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_frequency_pair_amd as atw
+from rope_frequency_pair_amd import synth
+from tests.gpu_util import BF16_TOL, max_err, sample_rows, say, sync, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL_LLAMA3 = {"rope_type": "llama3", "factor": 4.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+                "original_max_position_embeddings": 256}
+
+
+def _random_selection(batch, h_q, n_q, n_kv, seed, density, empty_block=None):
+    n_qb, n_kb = -(-n_q // 64), -(-n_kv // 64)
+    sel = torch.from_numpy(np.random.default_rng(seed).random((batch, h_q, n_qb, n_kb)) < density)
+    if empty_block is not None and empty_block < n_qb:
+        sel[:, :, empty_block] = False
+    return sel
+
+
+CASES = [
+    # d, h_q, h_kv, n_q, n_kv, q_pos0, causal, k_turns, density
+    (128, 6, 2, 700, 700, 0, True, 0.5, 0.35),
+    (64, 7, 1, 1000, 1000, 0, True, 2.0, 0.3),
+    (128, 4, 4, 300, 900, 600, True, 1.0, 0.5),
+    (64, 4, 2, 500, 530, 0, False, 1.0, 0.4),
+]
+
+
+@pytest.mark.parametrize("d,h_q,h_kv,n_q,n_kv,q_pos0,causal,k_turns,density", CASES)
+def test_sparse_prefill_parity(d, h_q, h_kv, n_q, n_kv, q_pos0, causal, k_turns, density):
+    say(f"sparse prefill d={d} heads {h_q}/{h_kv} n_q={n_q} n_kv={n_kv} q_pos0={q_pos0} causal={causal}")
+    q, k, v = synth.prefill_inputs(2, h_q, h_kv, n_q, n_kv, d, torch.bfloat16, 60 + d, device="cuda")
+    sel = _random_selection(2, h_q, n_q, n_kv, 61 + n_q, density, empty_block=2)
+    mask = atw.pack_block_mask(sel).cuda()
+    ref_args = (to_np(q), to_np(k), to_np(v), q_pos0, 1e4, k_turns)
+    for window_on in (True, False):
+        out = atw.prefill_sparse(q, k, v, mask, rope_base=1e4, k_turns=k_turns, q_pos0=q_pos0,
+                                 causal=causal, window_on=window_on)
+        sync()
+        ref = oracle.prefill(*ref_args, causal=causal, window_on=window_on, key_blocks=sel.numpy())
+        got = to_np(out)
+        err = max_err(got, ref)
+        say(f"  window_on={window_on} max abs err {err:.3e}")
+        assert np.isfinite(got).all() and err <= BF16_TOL
+        # a query block that attends nothing gives exactly 0
+        assert np.all(got[:, :, 128:192] == 0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_all_blocks_selected_is_dense_bitwise(d):
+    say(f"sparse all-selected == dense, d={d}")
+    q, k, v = synth.prefill_inputs(1, 4, 2, 900, 900, d, torch.bfloat16, 62, device="cuda")
+    sel = torch.ones((1, 4, -(-900 // 64), -(-900 // 64)), dtype=torch.bool)
+    mask = atw.pack_block_mask(sel).cuda()
+    for k_turns in (0.3, 4.0):
+        a = atw.prefill_sparse(q, k, v, mask, rope_base=1e4, k_turns=k_turns)
+        b = atw.prefill(q, k, v, rope_base=1e4, k_turns=k_turns)
+        sync()
+        assert torch.equal(a, b)
+
+
+def test_sparse_prefill_rope_scaling():
+    say("sparse prefill with llama3 rope scaling")
+    q, k, v = synth.prefill_inputs(1, 4, 2, 600, 600, 128, torch.bfloat16, 63, device="cuda")
+    sel = synth.block_selection(1, 4, 600, 600, 64, density=0.3, local=2)
+    mask = atw.pack_block_mask(sel).cuda()
+    out = atw.prefill_sparse(q, k, v, mask, rope_base=1e4, k_turns=0.6, rope_scaling=SMALL_LLAMA3)
+    sync()
+    ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, 0.6, scaling=SMALL_LLAMA3,
+                         key_blocks=sel.numpy())
+    err = max_err(to_np(out), ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_sparse_llama_128k_sampled_rows():
+    """The benchmark's 128K block-sparse workload (sink + local band + 10% of
+    earlier blocks), sampled rows of two heads against the oracle."""
+    w = synth.WORKLOADS["llama-3.2-3b-128k"]
+    say("sparse 128k: inputs and selection")
+    q, k, v = synth.workload_prefill_inputs(w)
+    sel = synth.block_selection(w.batch, w.h_q, w.n, w.n, w.seed + 100)
+    mask = atw.pack_block_mask(sel).cuda()
+    say("sparse 128k: running")
+    out = atw.prefill_sparse(q, k, v, mask, rope_base=w.rope_base, k_turns=w.k_turns)
+    sync()
+    heads = [0, 23]
+    G = w.h_q // w.h_kv
+    kvs = sorted({h // G for h in heads})
+    hmap = [kvs.index(h // G) for h in heads]
+    rows = sample_rows(w.n, seed=w.seed, count=3)
+    qn = to_np(q[:, heads][:, :, rows])
+    kn, vn = to_np(k[:, kvs]), to_np(v[:, kvs])
+    seln = sel[:, heads].numpy()
+    say(f"sparse 128k: oracle on {len(rows)} rows x {len(heads)} heads")
+    ref = np.zeros((1, len(heads), len(rows), w.head_dim))
+    for i, r in enumerate(rows):
+        n_kb = r // 64 + 1
+        kb_row = seln[:, :, r // 64:r // 64 + 1, :n_kb]
+        ref[:, :, i] = oracle.prefill(qn[:, :, i:i + 1], kn[:, :, :r + 1], vn[:, :, :r + 1], r,
+                                      w.rope_base, w.k_turns, kv_head_of_q=hmap,
+                                      key_blocks=kb_row)[:, :, 0]
+    err = max_err(to_np(out[:, heads][:, :, rows]), ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= BF16_TOL

@@ -227,3 +227,61 @@ def test_rope_scaling_rejected(lib, bad):
     with pytest.raises(atw.AtwError) as e:
         atw.window_widths(8, 1e4, 1.0, True, bad)
     assert e.value.code == binding.ATW_EINVAL
+
+
+def _packed_rows(sel):
+    """Pack a boolean [n_qb, n_kb] block selection into uint32 words (LSB first)."""
+    n_qb, n_kb = sel.shape
+    words = -(-n_kb // 32)
+    out = np.zeros((n_qb, words), dtype=np.uint32)
+    for kb in range(n_kb):
+        out[:, kb // 32] |= sel[:, kb].astype(np.uint32) << np.uint32(kb % 32)
+    return out
+
+
+@pytest.mark.parametrize("n_q,n_kv,q_pos0,causal,d,base,k", [
+    (700, 700, 0, True, 64, 1e4, 2.0), (300, 2100, 1800, True, 128, 5e5, 8.0),
+    (257, 3000, 0, False, 64, 1e6, 0.5), (64 * 40, 64 * 40, 0, True, 128, 1e7, 8.0),
+    (1, 5000, 4999, True, 128, 1e7, 8.0)])
+def test_sparse_counts_bit_exact(lib, n_q, n_kv, q_pos0, causal, d, base, k):
+    n_qb, n_kb = -(-n_q // 64), -(-n_kv // 64)
+    sel = np.random.default_rng(n_q + n_kv).random((n_qb, n_kb)) < 0.35
+    packed = _packed_rows(sel)
+    assert packed.shape[1] == lib.atw_block_mask_words(n_kv)
+    c64 = ctypes.c_int64
+    p, t = c64(), c64()
+    r = binding.rope_descriptor(base, None)
+    assert lib.atw_pruned_terms_sparse(n_q, n_kv, q_pos0, d, ctypes.byref(r), k, int(causal), 1,
+                                       packed.ctypes.data_as(ctypes.c_void_p), ctypes.byref(p),
+                                       ctypes.byref(t)) == 0
+    assert (p.value, t.value) == oracle.pruned_terms_blocks(n_q, n_kv, q_pos0, d, base, k, sel, causal)
+    # the torch packing helper gives the same words
+    import torch
+    words = atw.pack_block_mask(torch.tensor(sel)).numpy().view(np.uint32)
+    assert np.array_equal(words, packed)
+    # every block selected: the dense count
+    full = _packed_rows(np.ones((n_qb, n_kb), dtype=bool))
+    assert lib.atw_pruned_terms_sparse(n_q, n_kv, q_pos0, d, ctypes.byref(r), k, int(causal), 1,
+                                       full.ctypes.data_as(ctypes.c_void_p), ctypes.byref(p),
+                                       ctypes.byref(t)) == 0
+    assert (p.value, t.value) == atw.pruned_terms(n_q, n_kv, q_pos0, d, base, k, causal)
+
+
+def test_sparse_invalid_arguments(lib):
+    s = binding._arr64([0, 0, 0])
+    fake = ctypes.c_void_p(16)
+    r = binding.rope_descriptor(1e4, None)
+
+    def pre(dtype=1, mask=fake, d=128):
+        return lib.atw_prefill_sparse(fake, fake, fake, fake, dtype, 1, 10, 10, 0, 4, 2, None, d, s, s, s,
+                                      s, ctypes.byref(r), 4.0, 1, 1, 0.0, mask, fake, 1 << 40, None)
+
+    assert pre(dtype=0) == atw.binding.ATW_EUNSUPPORTED        # fp32: dense path only
+    assert pre(mask=None) == atw.binding.ATW_EINVAL
+    assert pre(mask=ctypes.c_void_p(18)) == atw.binding.ATW_EINVAL
+    assert pre(d=96) == atw.binding.ATW_EUNSUPPORTED
+    assert lib.atw_block_mask_words(0) == 0 and lib.atw_block_mask_words(64 * 32) == 1
+    assert lib.atw_block_mask_words(64 * 32 + 1) == 2
+    p, t = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.atw_pruned_terms_sparse(10, 10, 0, 64, ctypes.byref(r), 4.0, 1, 1, None, ctypes.byref(p),
+                                       ctypes.byref(t)) == atw.binding.ATW_EINVAL

@@ -291,8 +291,8 @@ def test_planted_boundary_mistake_is_caught(monkeypatch):
 def test_planted_scale_mistake_is_caught(monkeypatch):
     real = attention._row_output
 
-    def no_scale(q_hat, q_pos, k_hat, v, k_pos, widths, scale, causal):
-        return real(q_hat, q_pos, k_hat, v, k_pos, widths, 1.0, causal)
+    def no_scale(q_hat, q_pos, k_hat, v, k_pos, widths, scale, causal, allowed=None):
+        return real(q_hat, q_pos, k_hat, v, k_pos, widths, 1.0, causal, allowed)
 
     monkeypatch.setattr(attention, "_row_output", no_scale)
     with pytest.raises(AssertionError):
