@@ -426,6 +426,46 @@ def main():
             "on_vs_row_layout_off": round(result["decode_512k"]["ms_off"] / ma, 3),
             "line_bytes_on": by_line}
 
+        # the window on top of a page-level block selection in decode (first
+        # block, the last four blocks and 5% of the rest, per (sequence, kv
+        # head)), banded cache
+        dsel = synth.decode_block_selection(wd.batch, wd.h_kv, L, wd.seed + 100)
+        dmask = atw.pack_block_mask(dsel).to(dev)
+        del dsel
+
+        def sdstep(on):
+            atw.decode_sparse(qd, kb, vc, [L] * wd.batch, [L] * wd.batch, dmask, rope_base=wd.rope_base,
+                              k_turns=wd.k_turns, window_on=on, num_splits=wd.splits, k_banded=True,
+                              workspace=ws, out=od)
+
+        for _ in range(3):
+            sdstep(True)
+            sdstep(False)
+        a, b = [], []
+        for _ in range(10):
+            a += time_launches(lambda: sdstep(True), stream, 1)
+            b += time_launches(lambda: sdstep(False), stream, 1)
+        sb_on = sb_off = keys = 0
+        for bi in range(wd.batch):
+            for h in range(wd.h_kv):
+                pr, tot = atw.pruned_terms_sparse(1, L, L, wd.head_dim, wd.rope_base, wd.k_turns,
+                                                  dmask[bi, h][None])
+                n_keys = tot // (wd.head_dim // 2)
+                keys += n_keys
+                sb_on += 4 * (tot - pr) + 2 * wd.head_dim * n_keys
+                sb_off += 4 * tot + 2 * wd.head_dim * n_keys
+        ma, mb = statistics.median(a), statistics.median(b)
+        result["decode_512k_block_sparse_banded"] = {
+            "selection": "64-key blocks: first, last four and 5% of the rest per (sequence, kv head)",
+            "key_fraction": round(keys / (L * wd.h_kv * wd.batch), 4),
+            "ms_on": round(ma, 4), "ms_off": round(mb, 4), "on_off_speedup": round(mb / ma, 3),
+            "gbs_algorithmic_on": round(sb_on / (ma * 1e-3) / 1e9, 1),
+            "gbs_algorithmic_off": round(sb_off / (mb * 1e-3) / 1e9, 1),
+            "hbm_frac_on": round(sb_on / (ma * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_on": sb_on, "bytes_off": sb_off,
+            "speedup_vs_dense_banded_on": round(result["decode_512k_banded"]["ms_on"] / ma, 2)}
+        del dmask
+
         # multi-token decode (draft tokens verified in one step) on the same
         # banded cache: T tokens per sequence at positions L-T .. L-1
         multi = {}

@@ -151,6 +151,34 @@ int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cac
                            void* stream);
 
 /*
+ * atw_decode_sparse -- atw_decode_rope (k_banded = 0: row-layout K cache) or
+ * atw_decode_banded_rope (k_banded = 1) composed with a block-sparse key
+ * selection, as token-level selection methods make for decoding (the window
+ * applies on top of them: "ATFlash: Per-RoPE-Wavelength Attention Windows
+ * for Compute/Memory-Efficient LLM Inference", arXiv abstract).
+ *
+ *   block_mask: device uint32 [batch, h_kv, mask_words]: bit kb % 32 of word
+ *     kb / 32 set = the sequence's kv head (all query heads reading it)
+ *     attends keys [64 kb, 64 kb + 64).  Blocks at or beyond
+ *     ceil(kv_len / 64) are ignored.  Read only, 4-byte aligned.
+ *   mask_words: words per row, >= atw_block_mask_words(max kv_len).
+ *
+ * The split-KV partition divides each (sequence, kv head)'s selected blocks
+ * evenly over num_splits; unselected keys are never read.  A query head
+ * attending no key gets an output of 0.  One query token per sequence; every
+ * other argument, the workspace (atw_decode_workspace_bytes), the result
+ * codes and the limits as for atw_decode_rope.
+ */
+int atw_decode_sparse(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                      int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                      int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                      const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                      const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                      int32_t window_on, double softmax_scale, int32_t num_splits,
+                      const uint32_t* block_mask, int64_t mask_words, int32_t k_banded,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * atw_prefill -- windowed causal (or non-causal) attention for a block of
  * queries against a key/value sequence ("The idea": the window is a slice of
  * the query-key contraction axis; "Porting to something else": the pair loop

@@ -159,12 +159,16 @@ def prefill(q, k, v, q_pos0, rope_base, k_turns, causal=True, window_on=True, sc
 
 
 def decode(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal=True, window_on=True,
-           scale=None, kv_head_of_q=None, heads=None, batches=None, scaling=None):
+           scale=None, kv_head_of_q=None, heads=None, batches=None, scaling=None, key_blocks=None,
+           block=64):
     """Windowed attention output for single-token decode, float64.
 
     q: [B, Hq, d] (pre-RoPE, query of batch b at position q_pos[b]);
     k_cache, v_cache: [B, Hkv, Lmax, d] pre-RoPE, the first kv_len[b] keys of
     batch b valid, key j at position j.  Returns [len(batches), len(heads), d].
+    key_blocks: optional boolean [B, Hkv, n_blocks]: kv head h of sequence b
+    attends key j only if key_blocks[b, h, j // block] (a token-level
+    selection with the window on top); a head attending no key gives 0.
     """
     q = np.asarray(q)
     bsz, h_q, d = q.shape
@@ -185,10 +189,13 @@ def decode(q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causal=True, 
         for kvh, members in by_kv.items():
             k_hat = rope(k_cache[b, kvh, :n_kv], k_pos, theta)
             v64 = np.asarray(v_cache[b, kvh, :n_kv], dtype=np.float64)
+            allowed = None
+            if key_blocks is not None:
+                allowed = np.asarray(key_blocks[b, kvh])[k_pos // block]
             for hi, hq in members:
                 pos = int(q_pos[b])
                 q_hat = rope(q[b, hq][None, :], np.array([pos]), theta)[0]
-                out[bi, hi] = _row_output(q_hat, pos, k_hat, v64, k_pos, widths, scale, causal)
+                out[bi, hi] = _row_output(q_hat, pos, k_hat, v64, k_pos, widths, scale, causal, allowed)
     return out
 
 

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     decode_banded,
     decode_multi,
     decode_multi_workspace_bytes,
+    decode_sparse,
     kcache_band,
     pack_block_mask,
     decode_workspace_bytes,

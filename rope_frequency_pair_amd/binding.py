@@ -23,7 +23,7 @@ EXPORTED = [
     "atw_version", "atw_rope_theta", "atw_window_widths_rope", "atw_pruned_terms_rope",
     "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope", "atw_decode_multi",
     "atw_decode_multi_workspace_bytes", "atw_prefill_sparse", "atw_block_mask_words",
-    "atw_pruned_terms_sparse",
+    "atw_pruned_terms_sparse", "atw_decode_sparse",
 ]
 
 SPARSE_BLOCK = 64
@@ -146,6 +146,9 @@ def load_library(path=LIB_PATH):
     lib.atw_block_mask_words.restype = ctypes.c_int64
     lib.atw_pruned_terms_sparse.argtypes = [_i64, _i64, _i64, _i32, _prope, _f64, _i32, _i32, _vp, _pi64, _pi64]
     lib.atw_pruned_terms_sparse.restype = ctypes.c_int
+    lib.atw_decode_sparse.argtypes = (lib.atw_decode_rope.argtypes[:22] + [_vp, _i64, _i32] +
+                                      lib.atw_decode_rope.argtypes[22:])
+    lib.atw_decode_sparse.restype = ctypes.c_int
     lib.atw_last_error.argtypes = []
     lib.atw_last_error.restype = ctypes.c_char_p
     lib.atw_version.argtypes = []
@@ -445,6 +448,41 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
         _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
         _arr64(out.stride()[:2]), rope_arg, float(k_turns), int(causal), int(window_on),
         float(scale or 0.0), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return out
+
+
+def decode_sparse(q, k_cache, v_cache, kv_len, q_pos, block_mask, *, rope_base, k_turns, causal=True,
+                  window_on=True, scale=None, num_splits=64, kv_head_of_q=None, k_banded=False,
+                  workspace=None, out=None, stream=None, rope_scaling=None):
+    """decode() / decode_banded() restricted to a block-sparse key selection:
+    block_mask is the packed int32 device tensor [B, Hkv, words] (pack_block_mask
+    of a boolean [B, Hkv, n_blocks]), words >= block_mask_words(max kv_len)."""
+    import torch
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_banded and (k_cache.dim() != 5 or k_cache.shape[-1] != 16 or k_cache.stride(3) != 16):
+        raise ValueError("k_banded: k_cache must be [B, Hkv, d/16, L, 16] with token stride 16")
+    if (block_mask.dtype != torch.int32 or block_mask.dim() != 3 or tuple(block_mask.shape[:2]) != (B, Hkv)
+            or not block_mask.is_contiguous() or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be a contiguous int32 tensor [{B}, {Hkv}, words] on {q.device}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    need = lib.atw_decode_workspace_bytes(B, Hq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
+    q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
+    rdesc = rope_descriptor(rope_base, rope_scaling)
+    _check(lib.atw_decode_sparse(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
+        _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
+        _arr64(out.stride()[:2]), ctypes.byref(rdesc), float(k_turns), int(causal), int(window_on),
+        float(scale or 0.0), int(num_splits), ctypes.c_void_p(block_mask.data_ptr()),
+        int(block_mask.shape[2]), int(bool(k_banded)), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return out
 

@@ -2,6 +2,7 @@
 // planner, and the kernel launches.  Nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -441,7 +442,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
                 const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
                 const int64_t* o_strides, const double* theta, double k_turns, int32_t causal,
                 int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
-                size_t workspace_bytes, void* stream, bool banded) {
+                size_t workspace_bytes, void* stream, bool banded, const uint32_t* block_mask = nullptr,
+                int64_t mask_words = 0, bool sparse = false) {
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "decode supports head_dim 64 and 128 (got %d)", head_dim);
   if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 only");
@@ -460,6 +462,16 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
       return fail(ATW_EINVAL, "causal decode needs q_pos[%lld] + q_len - 1 >= kv_len - 1", (long long)b);
     if (q_pos[b] + q_len - 1 >= (int64_t(1) << 30))
       return fail(ATW_EINVAL, "q_pos[%lld] + q_len - 1 out of range", (long long)b);
+  }
+  if (sparse) {
+    if (block_mask == nullptr) return fail(ATW_EINVAL, "block_mask is NULL");
+    if (reinterpret_cast<uintptr_t>(block_mask) % 4 != 0) return fail(ATW_EINVAL, "block_mask must be 4-byte aligned");
+    if (q_len != 1) return fail(ATW_EUNSUPPORTED, "block-sparse decode takes one query token per sequence");
+    int64_t max_len = 0;
+    for (int64_t b = 0; b < batch; ++b) max_len = std::max(max_len, kv_len[b]);
+    if (mask_words < atw_block_mask_words(max_len) || mask_words > (int64_t(1) << 24))
+      return fail(ATW_EINVAL, "mask_words must be >= atw_block_mask_words(max kv_len) (%lld)",
+                  (long long)atw_block_mask_words(max_len));
   }
   int16_t kvh[atw::kMaxHeadsQ];
   if (int e = check_heads(h_q, h_kv, kv_head_of_q, kvh)) return e;
@@ -519,6 +531,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   }
   p.kv_first[h_kv] = (int16_t)n;
   p.group = h_q / h_kv;
+  if (sparse) {
+    p.sel = block_mask;
+    p.sel_words = (int32_t)mask_words;
+  }
   fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
   return hip_status(atw::launch_decode(p, head_dim, banded, (hipStream_t)stream), "decode launch");
 }
@@ -589,6 +605,22 @@ int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cac
                      head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
+}
+
+int atw_decode_sparse(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                      int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                      int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                      const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                      const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
+                      int32_t window_on, double softmax_scale, int32_t num_splits,
+                      const uint32_t* block_mask, int64_t mask_words, int32_t k_banded,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  double theta[atw::kMaxHeadDim / 2];
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal,
+                     window_on, softmax_scale, num_splits, workspace, workspace_bytes, stream,
+                     k_banded != 0, block_mask, mask_words, true);
 }
 
 size_t atw_decode_multi_workspace_bytes(int64_t batch, int32_t q_len, int32_t h_q, int32_t head_dim,

@@ -105,6 +105,66 @@ __device__ void split_range(int kv_len, int qpos, bool causal, int splits, int s
   *k_end = bound(split + 1);
 }
 
+// Block-sparse selection: the range of selected key blocks split `split` of
+// `splits` takes (splits carry equal numbers of selected blocks).  row holds
+// n_words mask words; blocks at or beyond nb are ignored.  Wave-wide: lanes
+// read 64 words at a time, count bits, and a prefix scan over lanes finds
+// the word and bit of the split's first block.  Returns the number of blocks
+// and the position (word, bit) of the first.
+__device__ __forceinline__ uint32_t valid_bits(int word, int nb) {
+  const int rest = nb - 32 * word;
+  return rest >= 32 ? 0xffffffffu : (rest <= 0 ? 0u : ((1u << rest) - 1u));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ void sparse_split(const uint32_t* row, int n_words, int nb, int splits, int split,
+                             int* first_word, int* first_bit, int* count) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int base = 0; base < n_words; base += 64) {
+    const int wi = base + lane;
+    const uint32_t w = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
+    total += wave_sum_i32(__popc(w));
+  }
+  const int lo = (int)((int64_t)total * split / splits);
+  const int hi = (int)((int64_t)total * (split + 1) / splits);
+  *count = hi - lo;
+  *first_word = n_words;
+  *first_bit = 0;
+  if (hi <= lo) return;
+  int before = 0;
+  for (int base = 0; base < n_words; base += 64) {
+    const int wi = base + lane;
+    const uint32_t w = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
+    const int c = __popc(w);
+    int incl = c;                                   // inclusive prefix over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - c;
+    const bool here = lo >= before + excl && lo < before + incl;
+    const uint64_t hit = __ballot(here);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      // the (lo - before - excl)-th set bit of this lane's word
+      uint32_t rest = w;
+      for (int k = lo - before - excl; k > 0 && rest; --k) rest &= rest - 1u;
+      const int bit = rest ? __builtin_ctz(rest) : 0;
+      *first_word = __shfl(wi, src);
+      *first_bit = __shfl(bit, src);
+      return;
+    }
+    before += __shfl(incl, 63);
+  }
+}
+
 template <int D>
 struct DSmem {
   __bf16 k[kTK][DCfg<D>::KROW];
@@ -125,7 +185,7 @@ struct DSmem {
 // recomputed token by token from the rotated values kept in registers, each
 // lane keeping its own token's scores.  Keys after a token's position are
 // masked out of that token's column.
-template <int D, bool BANDED, bool MULTI>
+template <int D, bool BANDED, bool MULTI, bool SPARSE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(const DecodeParams p) {
   using C = DCfg<D>;
   constexpr int H = C::H;
@@ -136,8 +196,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const int kv_len = p.kv_len[b];
   const int qpos = p.q_pos[b];
   const bool causal = p.causal != 0;
-  int k_begin, k_end;
-  split_range<D, BANDED>(kv_len, qpos, causal, p.splits, split, p.win.w, &k_begin, &k_end);
+  int k_begin = 0, k_end = kv_len;
+  // SPARSE: this split's selected key blocks, walked 32 at a time
+  const uint32_t* sel_row = nullptr;
+  int sel_word = 0, sel_left = 0;
+  uint32_t sel_bits = 0;
+  const int n_blocks = (kv_len + kSparseBlock - 1) / kSparseBlock;
+  if constexpr (SPARSE) {
+    sel_row = p.sel + ((int64_t)b * p.h_kv + kvh) * p.sel_words;
+    int first_bit = 0;
+    sparse_split(sel_row, min(p.sel_words, (n_blocks + 31) / 32), n_blocks, p.splits, split, &sel_word,
+                 &first_bit, &sel_left);
+    sel_word = __builtin_amdgcn_readfirstlane(sel_word);
+    first_bit = __builtin_amdgcn_readfirstlane(first_bit);
+    sel_left = __builtin_amdgcn_readfirstlane(sel_left);
+    if (sel_left > 0)
+      sel_bits = __builtin_amdgcn_readfirstlane(sel_row[sel_word]) & valid_bits(sel_word, n_blocks) &
+                 (0xffffffffu << first_bit);
+  } else {
+    split_range<D, BANDED>(kv_len, qpos, causal, p.splits, split, p.win.w, &k_begin, &k_end);
+  }
 
   const int g0 = p.kv_first[kvh], G = p.kv_first[kvh + 1] - g0;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
@@ -205,8 +283,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     return (causal || d >= 0) ? d : -d;
   };
 
-  auto load_tile = [&](int t) {
-    const int m0 = k_begin + t * kTK;
+  auto load_tile = [&](int m0) {
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
       const int m = m0 + C::KPR * i + kj;
@@ -248,13 +325,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // last token
   uint32_t rot[MULTI ? C::ROUNDS : 1][8];
   bool nonuni = false;
-  auto store_tile = [&](int t) {
-    const int m0 = k_begin + t * kTK;
+  auto store_tile = [&](int m0) {
     nonuni = false;
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
       const int m = m0 + C::KPR * i + kj;
-      if (round_ix % kReanchorRounds == 0) {
+      // exact angles every kReanchorRounds rounds, and (sparse) at the start
+      // of every selected block, after which keys are no longer consecutive
+      const bool anchor = SPARSE ? (i == 0 && (m0 & (kSparseBlock - 1)) == 0)
+                                 : (round_ix % kReanchorRounds == 0);
+      if (anchor) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) rope_sincos(m, p.win.phi[kc * 8 + e], &rs[e], &rc[e]);
       }
@@ -293,8 +373,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   };
 
   // MULTI: rewrite the staged K' tile windowed for token j (distance + j)
-  auto rewrite_k = [&](int t, int j) {
-    const int m0 = k_begin + t * kTK;
+  auto rewrite_k = [&](int m0, int j) {
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
       const int m = m0 + C::KPR * i + kj;
@@ -311,14 +390,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   };
 
-  if (n_tiles > 0) load_tile(0);
+  // tiles visited: dense, the split's consecutive tiles; sparse, the two
+  // 32-key halves of each selected block (the second only if it holds keys)
+  int t_dense = -1;
+  int half = 1, cur_block = -1;
+  auto next_tile = [&]() -> int {
+    if constexpr (!SPARSE) {
+      ++t_dense;
+      return t_dense < n_tiles ? k_begin + t_dense * kTK : -1;
+    } else {
+      if (half == 0 && kSparseBlock * cur_block + kTK < kv_len) {
+        half = 1;
+        return kSparseBlock * cur_block + kTK;
+      }
+      if (sel_left == 0) return -1;
+      while (sel_bits == 0) {
+        ++sel_word;
+        sel_bits = __builtin_amdgcn_readfirstlane(sel_row[sel_word]) & valid_bits(sel_word, n_blocks);
+      }
+      cur_block = 32 * sel_word + __builtin_ctz(sel_bits);
+      sel_bits &= sel_bits - 1u;
+      --sel_left;
+      half = 0;
+      return kSparseBlock * cur_block;
+    }
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    store_tile(t);
+  int m_cur = next_tile();
+  if (m_cur >= 0) load_tile(m_cur);
+
+  while (m_cur >= 0) {
+    store_tile(m_cur);
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int m_next = next_tile();
+    if (m_next >= 0) load_tile(m_next);
 
-    const int m_lo = k_begin + t * kTK;
+    const int m_lo = m_cur;
     const int m_hi = min(m_lo + kTK - 1, k_end - 1);
     int64_t dmin = 0, dmax = 0;
     tile_distance_range(qpos, qpos, m_lo, m_hi, causal, &dmin, &dmax);
@@ -346,7 +453,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         // recompute for each later token from the rotated values
         for (int j = 1; j < q_len; ++j) {
           __syncthreads();
-          rewrite_k(t, j);
+          rewrite_k(m_cur, j);
           __syncthreads();
           f32x4 sj[2];
           qk(sj);
@@ -416,6 +523,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       oacc[bd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, oacc[bd], 0, 0, 0);
     }
     __syncthreads();   // LDS reads done before the next store
+    m_cur = m_next;
   }
 
   // partial result of this split: [m (raw score units), l, -, -, o[D]] per query head
@@ -491,7 +599,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
 #pragma unroll
     for (int i = 0; i < G - 1; ++i) acc += gsum[i][d];
     __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1] + tok * p.os[2];
-    o[d] = (__bf16)(acc / l);
+    o[d] = (__bf16)(l > 0.f ? acc / l : 0.f);   // no attended key: 0
   }
 }
 
@@ -518,25 +626,30 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipSt
   dim3 grid((unsigned)p.splits, (unsigned)p.h_kv, (unsigned)p.batch);
   dim3 cgrid((unsigned)p.h_q, (unsigned)(p.batch * p.q_len));
   const bool multi = p.q_len > 1;
-#define ATW_DECODE_SPLIT(DD, BB, MM) \
-  hipLaunchKernelGGL((decode_split_kernel<DD, BB, MM>), grid, dim3(64), 0, stream, p)
+  const bool sparse = p.sel != nullptr;
+  if (multi && sparse) return hipErrorInvalidValue;
+#define ATW_DECODE_SPLIT(DD, BB, MM, SS) \
+  hipLaunchKernelGGL((decode_split_kernel<DD, BB, MM, SS>), grid, dim3(64), 0, stream, p)
+#define ATW_DECODE_ALL(DD)                                                         \
+  if (sparse) {                                                                    \
+    if (banded) ATW_DECODE_SPLIT(DD, true, false, true);                           \
+    else ATW_DECODE_SPLIT(DD, false, false, true);                                 \
+  } else if (multi) {                                                              \
+    if (banded) ATW_DECODE_SPLIT(DD, true, true, false);                           \
+    else ATW_DECODE_SPLIT(DD, false, true, false);                                 \
+  } else {                                                                         \
+    if (banded) ATW_DECODE_SPLIT(DD, true, false, false);                          \
+    else ATW_DECODE_SPLIT(DD, false, false, false);                                \
+  }                                                                                \
+  hipLaunchKernelGGL((decode_combine_kernel<DD>), cgrid, dim3(kCombineThreads), 0, stream, p)
   if (head_dim == 128) {
-    if (multi) {
-      if (banded) ATW_DECODE_SPLIT(128, true, true); else ATW_DECODE_SPLIT(128, false, true);
-    } else {
-      if (banded) ATW_DECODE_SPLIT(128, true, false); else ATW_DECODE_SPLIT(128, false, false);
-    }
-    hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(kCombineThreads), 0, stream, p);
+    ATW_DECODE_ALL(128);
   } else if (head_dim == 64) {
-    if (multi) {
-      if (banded) ATW_DECODE_SPLIT(64, true, true); else ATW_DECODE_SPLIT(64, false, true);
-    } else {
-      if (banded) ATW_DECODE_SPLIT(64, true, false); else ATW_DECODE_SPLIT(64, false, false);
-    }
-    hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(kCombineThreads), 0, stream, p);
+    ATW_DECODE_ALL(64);
   } else {
     return hipErrorInvalidValue;
   }
+#undef ATW_DECODE_ALL
 #undef ATW_DECODE_SPLIT
   return hipGetLastError();
 }

@@ -52,6 +52,11 @@ struct DecodeParams {
   int64_t qs[3], ks[3], vs[3], os[3];   // q / o: (batch, head, token) element strides
   int32_t batch, h_q, h_kv, splits;
   int32_t causal, group, q_len, pad1;   // group = query heads per kv head; q_len tokens per sequence
+  // Block-sparse key selection (nullptr: every key): bit kb % 32 of word
+  // kb / 32 of row (b * h_kv + kvh), rows of sel_words words: the sequence's
+  // kv head attends key block kb (64 keys).
+  const uint32_t* sel;
+  int32_t sel_words, pad2;
   float scale_log2;
   int32_t kv_len[kMaxDecodeBatch];
   int32_t q_pos[kMaxDecodeBatch];

@@ -139,3 +139,22 @@ def block_selection(batch, h_q, n_q, n_kv, seed, density=0.1, sink=1, local=4, b
     band = (kb <= diag) & (kb > diag - local)
     sel |= (band | (kb < sink))[None, None]
     return torch.from_numpy(sel)
+
+
+def decode_block_selection(batch, h_kv, kv_len, seed, density=0.05, sink=1, local=4, block=64):
+    """Seeded boolean key-block selection for decode [batch, h_kv,
+    ceil(max(kv_len)/block)]: the first `sink` blocks, the last `local` blocks
+    of each sequence's keys, and every other block with probability
+    `density`, independently per (sequence, kv head) -- the shape of a
+    page-level top-k selection.  numpy PCG64 seeded with `seed`."""
+    import numpy as np
+    lens = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * batch)]
+    n_kb = -(-max(lens) // block)
+    rng = np.random.default_rng(seed)
+    sel = rng.random((batch, h_kv, n_kb), dtype=np.float32) < density
+    kb = np.arange(n_kb)
+    for b, n in enumerate(lens):
+        last = -(-n // block)
+        sel[b, :, kb >= last] = False
+        sel[b, :, (kb < sink) | ((kb >= last - local) & (kb < last))] = True
+    return torch.from_numpy(sel)

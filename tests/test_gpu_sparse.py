@@ -117,3 +117,67 @@ def test_sparse_llama_128k_sampled_rows():
     err = max_err(to_np(out[:, heads][:, :, rows]), ref)
     say(f"  max abs err {err:.3e}")
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("splits", [7, 64])
+@pytest.mark.parametrize("banded", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_sparse_decode_parity(d, banded, splits):
+    say(f"sparse decode d={d} banded={banded} splits={splits}")
+    kv_len = [3000, 1777, 64]
+    q, kc, vc = synth.decode_inputs(3, 8, 2, 3000, d, torch.bfloat16, 70 + d, device="cuda")
+    sel = synth.decode_block_selection(3, 2, kv_len, 71, density=0.3, local=2)
+    sel[1, 1] = False                      # a (sequence, kv head) that attends nothing
+    mask = atw.pack_block_mask(sel).cuda()
+    kin = atw.kcache_band(kc) if banded else kc
+    for window_on, k_turns in ((True, 0.7), (True, 4.0), (False, 1.0)):
+        out = atw.decode_sparse(q, kin, vc, kv_len, [n - 1 for n in kv_len], mask, rope_base=1e4,
+                                k_turns=k_turns, window_on=window_on, num_splits=splits, k_banded=banded)
+        sync()
+        ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, [n - 1 for n in kv_len], 1e4, k_turns,
+                            window_on=window_on, key_blocks=sel.numpy())
+        got = to_np(out)
+        err = max_err(got, ref)
+        say(f"  window_on={window_on} k={k_turns} max abs err {err:.3e}")
+        assert np.isfinite(got).all() and err <= BF16_TOL
+        assert np.all(got[1, 4:] == 0.0)
+
+
+def test_sparse_decode_all_selected_matches_dense():
+    """Every block selected: the dense decode's result (within rounding: the
+    split partition differs)."""
+    q, kc, vc = synth.decode_inputs(2, 14, 2, 2500, 128, torch.bfloat16, 72, device="cuda")
+    sel = torch.ones((2, 2, -(-2500 // 64)), dtype=torch.bool)
+    mask = atw.pack_block_mask(sel).cuda()
+    a = atw.decode_sparse(q, kc, vc, [2500, 900], [2499, 899], mask, rope_base=1e6, k_turns=2.0, num_splits=16)
+    b = atw.decode(q, kc, vc, [2500, 900], [2499, 899], rope_base=1e6, k_turns=2.0, num_splits=16)
+    sync()
+    assert max_err(to_np(a), to_np(b).astype(np.float64)) <= BF16_TOL
+
+
+def test_sparse_decode_workload_512k_sampled():
+    """The 512K decode workload with a page-level selection (first block, last
+    four blocks, 5% of the rest per (sequence, kv head)), banded K cache."""
+    w = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+    say("sparse decode 512k: inputs")
+    q, kc, vc = synth.workload_decode_inputs(w)
+    L = w.n
+    sel = synth.decode_block_selection(w.batch, w.h_kv, L, w.seed + 100)
+    mask = atw.pack_block_mask(sel).cuda()
+    kb = atw.kcache_band(kc)
+    say("sparse decode 512k: running")
+    out = atw.decode_sparse(q, kb, vc, [L] * w.batch, [L] * w.batch, mask, rope_base=w.rope_base,
+                            k_turns=w.k_turns, num_splits=w.splits, k_banded=True)
+    sync()
+    del kb
+    G = w.h_q // w.h_kv
+    for b, kvh in ((0, 0), (5, 3)):
+        heads = list(range(kvh * G, (kvh + 1) * G))
+        qn = to_np(q[b:b + 1, heads])
+        kn, vn = to_np(kc[b:b + 1, kvh:kvh + 1]), to_np(vc[b:b + 1, kvh:kvh + 1])
+        say(f"sparse decode 512k: oracle b={b} kv={kvh}")
+        ref = oracle.decode(qn, kn, vn, [L], [L], w.rope_base, w.k_turns, kv_head_of_q=[0] * G,
+                            key_blocks=sel[b:b + 1, kvh:kvh + 1].numpy())
+        err = max_err(to_np(out[b:b + 1, heads]), ref)
+        say(f"  max abs err {err:.3e}")
+        assert err <= BF16_TOL

@@ -285,3 +285,22 @@ def test_sparse_invalid_arguments(lib):
     p, t = ctypes.c_int64(), ctypes.c_int64()
     assert lib.atw_pruned_terms_sparse(10, 10, 0, 64, ctypes.byref(r), 4.0, 1, 1, None, ctypes.byref(p),
                                        ctypes.byref(t)) == atw.binding.ATW_EINVAL
+
+
+def test_decode_sparse_invalid_arguments(lib):
+    s3, s2 = binding._arr64([0, 0, 0]), binding._arr64([0, 0])
+    fake = ctypes.c_void_p(16)
+    r = binding.rope_descriptor(1e4, None)
+    kv = binding._arr64([5000])
+    qp = binding._arr64([4999])
+
+    def dec(mask=fake, words=3, banded=0):
+        return lib.atw_decode_sparse(fake, fake, fake, fake, 1, 1, kv, qp, 4, 2, None, 128, s2, s3, s3, s2,
+                                     ctypes.byref(r), 4.0, 1, 1, 0.0, 8, mask, words, banded, fake, 1 << 30,
+                                     None)
+
+    assert lib.atw_block_mask_words(5000) == 3
+    assert dec(mask=None) == atw.binding.ATW_EINVAL
+    assert dec(mask=ctypes.c_void_p(18)) == atw.binding.ATW_EINVAL
+    assert dec(words=2) == atw.binding.ATW_EINVAL
+    assert b"mask_words" in lib.atw_last_error()

@@ -144,3 +144,26 @@ def test_block_counts_all_selected_equal_dense(n_q, n_kv, q_pos0, causal, block)
     assert a == oracle.pruned_terms(n_q, n_kv, q_pos0, 16, 50.0, 1.0, causal)
     none = np.zeros_like(sel)
     assert oracle.pruned_terms_blocks(n_q, n_kv, q_pos0, 16, 50.0, 1.0, none, causal, block=block) == (0, 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_decode_with_selection_equals_prefill_row(causal):
+    """The decode oracle with a per-(sequence, kv head) selection gives the
+    prefill oracle's row for the same query, keys and selection."""
+    d, base, k_turns, block = 32, 1e4, 1.0, 16
+    kv_len, h_q, h_kv = [150, 97], 4, 2
+    q = _rand((2, h_q, d), 51)
+    kc, vc = _rand((2, h_kv, 160, d), 52), _rand((2, h_kv, 160, d), 53)
+    sel = np.random.default_rng(54).random((2, h_kv, 10)) < 0.5
+    sel[1, 1] = False                                  # a head that attends nothing
+    q_pos = [149, 130]
+    out = oracle.decode(q, kc, vc, kv_len, q_pos, base, k_turns, causal=causal, key_blocks=sel, block=block)
+    for b in range(2):
+        for hq in range(h_q):
+            kvh = hq // (h_q // h_kv)
+            n = kv_len[b]
+            kb = sel[b, kvh][None, None, None, :-(-n // block)]
+            ref = oracle.prefill(q[b, hq][None, None, None], kc[b, kvh][None, None, :n], vc[b, kvh][None, None, :n],
+                                 q_pos[b], base, k_turns, causal=causal, key_blocks=kb, block=block)[0, 0, 0]
+            np.testing.assert_array_equal(out[b, hq], ref)
+    assert np.all(out[1, 2:] == 0.0)
