@@ -115,7 +115,7 @@ def time_launches(fn, stream, n):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def cpu_baseline(sample_rows=96):
+def cpu_baseline(sample_rows=256):
     """Time the fp64 oracle on a bounded sample of the headline workload."""
     import multiprocessing as mp
 
