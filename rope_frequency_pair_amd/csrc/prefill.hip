@@ -356,7 +356,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
     }
   };
 
-  // ---- prologue: the first tile in LDS
+  // ---- prologue: K' buffers zeroed (a K' block the window prunes for the
+  // whole workgroup is never copied, and is read only against a fully masked
+  // query operand, which needs finite data), then the first tile in LDS
+#pragma unroll
+  for (int i = 0; i < 2 * TILE / (8 * kThreads); ++i)
+    reinterpret_cast<u32x4*>(&lk[0][0])[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
   int t = -1, t_next = -1, slot = 0;
   bool own = false, own_next = false;
   next_tile(&t, &own);
@@ -402,8 +408,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       // of the k-steps are read before the branches (a block of a pruned
       // k-step holds stale data that is never used), the lower half once the
       // loop reaches it, so each MFMA waits only for its own reads.
-      const int kk0 = r_full >> 3;
-      if (kk0 < C::NKS) {
+      // (r_full == H, every pair partial or pruned: k-step NKS-1 with all its
+      // slots masked, which yields zero; its K' slot holds finite data, as
+      // the K' buffers start zeroed)
+      const int kk0 = min(r_full >> 3, C::NKS - 1);
+      {
         constexpr int HALF = C::NKS / 2;
         bf16x8 ka[C::NKS][2];
         if constexpr (D != 64) {
@@ -447,9 +456,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
             sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
           }
         }
-      } else {
-        sacc[0] = f32x16{};
-        sacc[1] = f32x16{};
       }
       // partially windowed pairs [r_any, r_full): one pair per MFMA into a
       // separate accumulator, ascending, each followed by the reset
