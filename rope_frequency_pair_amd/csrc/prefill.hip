@@ -35,13 +35,14 @@
 //  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
 //    k-step of 16 covers 8 whole pairs, so the retained pairs [r, h) are a
 //    contiguous range of k-steps;
-//  * per tile and wave: the k-step holding the first fully kept pair starts
-//    the accumulation (its partial slots masked out of the query operand),
-//    the fully kept k-steps above it follow; pairs that are in the window for
-//    some cells of the tile and not for others ("partial" pairs) go one pair
-//    per MFMA into a separate accumulator, and after each such pair the cells
-//    beyond its window are reset to zero; because windows grow with r, this
-//    leaves exactly the kept partial terms;
+//  * per tile and wave: pairs that are in the window for some cells of the
+//    tile and not for others ("partial" pairs) go one pair per MFMA, and
+//    after each such pair the cells beyond its window are reset to zero;
+//    because windows grow with r, this leaves exactly the kept partial terms
+//    (head_dim 64: first, in the score accumulator itself; head_dim 128: in a
+//    separate accumulator added afterwards); the k-step holding the first
+//    fully kept pair (its partial slots masked out of the query operand) and
+//    the fully kept k-steps above it complete the scores;
 //  * O^T += V^T P^T with P^T taken straight from the S^T registers (V is
 //    packed in the key order that register layout produces);
 //  * one workgroup barrier per tile; tile geometry (distances, pair ranges)
@@ -389,13 +390,23 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       auto drop_cells = [&](f32x16 (&x)[2], int pp) {
         int thr_lo, thr_hi;
         drop_bounds(npos, p.win.w[pp], kbase_lane, causal, kTK, &thr_lo, &thr_hi);
+        if (D == 64 && causal) {
+          // causal: only keys too far back are beyond the window (one compare
+          // per cell; at head_dim 128 the general form measured as fast)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int ko = 32 * blk + acc_row(v);
-            if (ko < thr_lo || ko > thr_hi) x[blk][v] = 0.f;
-          }
+            for (int v = 0; v < 16; ++v)
+              if (32 * blk + acc_row(v) < thr_lo) x[blk][v] = 0.f;
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int ko = 32 * blk + acc_row(v);
+              if (ko < thr_lo || ko > thr_hi) x[blk][v] = 0.f;
+            }
+        }
       };
       auto kop = [&](int ks, int blk) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(kt + blk_off(2 * ks + blk, lane));
@@ -422,14 +433,46 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
             ka[ks][1] = kop(ks, 1);
           }
         }
+        // query operand of k-step pp's pair alone (one-hot pair slot)
+        auto pair_op = [&](int pp) -> bf16x8 {
+          const int ks = pp >> 3, uu = pp & 7;
+          const uint32_t qd =
+              *reinterpret_cast<const uint32_t*>(qw_lds + blk_off(ks, lane) + 2 * (uu & 3));
+          const bool mine = sh == (uu >> 2);
+          u32x4 bw;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
+          return __builtin_bit_cast(bf16x8, bw);
+        };
         {
           u32x4 bw = *reinterpret_cast<const u32x4*>(qw_lds + blk_off(kk0, lane));
           const int tau = r_full - 8 * kk0 - 4 * sh;   // slots below tau are partial
 #pragma unroll
           for (int u = 0; u < 4; ++u) bw[u] = (u < tau) ? 0u : bw[u];
           const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, f32x16{}, 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
+          if (D == 64 && r_any < r_full) {
+            // partially windowed pairs [r_any, r_full) first, one pair per
+            // MFMA, ascending, each followed by the reset of the cells beyond
+            // its window (windows grow with r, so what remains is exactly the
+            // kept partial terms); then the masked k-step on top
+            {
+              const bf16x8 b0 = pair_op(r_any);
+              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(r_any >> 3, 0), b0, f32x16{}, 0, 0, 0);
+              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(r_any >> 3, 1), b0, f32x16{}, 0, 0, 0);
+              drop_cells(sacc, r_any);
+            }
+            for (int pp = r_any + 1; pp < r_full; ++pp) {
+              const bf16x8 bp = pair_op(pp);
+              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(pp >> 3, 0), bp, sacc[0], 0, 0, 0);
+              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(pp >> 3, 1), bp, sacc[1], 0, 0, 0);
+              drop_cells(sacc, pp);
+            }
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, sacc[1], 0, 0, 0);
+          } else {
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, f32x16{}, 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
+          }
         }
         if constexpr (D == 64) {
           // head_dim 64: operands read per k-step, query operand from the LDS
@@ -457,9 +500,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
           }
         }
       }
-      // partially windowed pairs [r_any, r_full): one pair per MFMA into a
-      // separate accumulator, ascending, each followed by the reset
-      if (r_any < r_full) {
+      // head_dim 128: partially windowed pairs [r_any, r_full) one pair per
+      // MFMA into a separate accumulator, ascending, each followed by the
+      // reset, then added (head_dim 64 handled them above, before the kept
+      // k-steps, in the same accumulator: no zeroing and no final add, which
+      // matters at its budget of 128 registers and vector-bound tile; at
+      // head_dim 128 the separate accumulator measured faster)
+      if (D != 64 && r_any < r_full) {
         f32x16 x[2] = {f32x16{}, f32x16{}};
         for (int pp = r_any; pp < r_full; ++pp) {
           const int ks = pp >> 3, uu = pp & 7;
