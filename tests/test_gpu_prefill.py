@@ -55,6 +55,21 @@ def test_bf16_ragged_gqa(d, k_turns):
     _run_and_compare(q, k, v, 1e4, k_turns, BF16_TOL)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_pair_pruned_in_far_tiles(d):
+    """Windows so short (k = 0.02) that beyond ~1000 positions every pair is
+    pruned: far cells score 0 and stay in the softmax; whole workgroups then
+    copy no K' block of a tile and read zeroed / stale K' slots against a fully
+    masked query operand."""
+    say(f"prefill bf16 every pair pruned far away, d={d}")
+    assert oracle.window_widths(d, 1e4, 0.02)[-1] < 1200
+    q, k, v = synth.prefill_inputs(1, 2, 1, 3000, 3000, d, torch.bfloat16, 16, device="cuda")
+    _run_and_compare(q, k, v, 1e4, 0.02, BF16_TOL)
+    # and the fp32 path
+    q, k, v = synth.prefill_inputs(1, 2, 1, 2100, 2100, d, torch.float32, 17, device="cuda")
+    _run_and_compare(q, k, v, 1e4, 0.02, F32_TOL)
+
+
 def test_fp32_ragged_d128_partial_pairs():
     say("prefill fp32 ragged d=128")
     q, k, v = synth.prefill_inputs(1, 2, 1, 333, 333, 128, torch.float32, 8, device="cuda")
