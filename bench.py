@@ -263,7 +263,7 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(flops_on / (kern_ms * 1e-3) / 1e12, 1),
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(flops_on / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                          "traffic": traffic, "kernel": "prefill_bf16_kernel<128, false>",
+                          "traffic": traffic, "kernel": "prefill_bf16_kernel<128, false, true>",
                           "kernel_ms_mean": round(kern_ms, 3), "kernel_sha": sha}
 
     if not (args.quick or args.on_only):

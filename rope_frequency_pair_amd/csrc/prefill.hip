@@ -46,7 +46,9 @@
 //  * O^T += V^T P^T with P^T taken straight from the S^T registers (V is
 //    packed in the key order that register layout produces);
 //  * one workgroup barrier per tile; tile geometry (distances, pair ranges)
-//    is wave-uniform and runs on the scalar unit;
+//    is wave-uniform and runs on the scalar unit; causal / non-causal and
+//    dense / block-sparse are separate instantiations, so neither is tested
+//    in the loop;
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
 //  * head_dim 64 asks for four waves per SIMD (two workgroups per CU: 64 KB
@@ -175,7 +177,7 @@ __device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, b
   return true;
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel(const PrefillParams p) {
   using C = PCfg<D>;
   constexpr int H = C::H;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
   const __bf16* kpk = (const __bf16*)p.kp + tix0 * TILE;
   const __bf16* vpk = (const __bf16*)p.vp + tix0 * TILE;
 
-  const bool causal = p.causal != 0;
+  constexpr bool causal = CAUSAL;
   const int n_kv = p.n_kv;
   const int i0 = qb * kPrefillBlockRows;
   const int g_last = min(i0 + kPrefillBlockRows - 1, p.n_q - 1);
@@ -390,9 +392,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       auto drop_cells = [&](f32x16 (&x)[2], int pp) {
         int thr_lo, thr_hi;
         drop_bounds(npos, p.win.w[pp], kbase_lane, causal, kTK, &thr_lo, &thr_hi);
-        if (D == 64 && causal) {
+        if constexpr (CAUSAL) {
           // causal: only keys too far back are beyond the window (one compare
-          // per cell; at head_dim 128 the general form measured as fast)
+          // per cell)
 #pragma unroll
           for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -618,21 +620,23 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int
   if (blocks <= 0) return hipSuccess;
   dim3 pgrid((unsigned)pk.n_kt, (unsigned)pk.h_kv, (unsigned)pk.batch);
   dim3 grid((unsigned)blocks), block(kThreads);
+#define ATW_PREFILL(DD)                                                                            \
+  hipLaunchKernelGGL(pack_kv_kernel<DD>, pgrid, dim3(256), 0, stream, pk);                           \
+  if (p.sel) {                                                                                       \
+    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<DD, true, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prefill_bf16_kernel<DD, true, false>), grid, block, 0, stream, p);      \
+  } else {                                                                                           \
+    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<DD, false, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prefill_bf16_kernel<DD, false, false>), grid, block, 0, stream, p);     \
+  }
   if (head_dim == 128) {
-    hipLaunchKernelGGL(pack_kv_kernel<128>, pgrid, dim3(256), 0, stream, pk);
-    if (p.sel)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p);
+    ATW_PREFILL(128);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL(pack_kv_kernel<64>, pgrid, dim3(256), 0, stream, pk);
-    if (p.sel)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, p);
+    ATW_PREFILL(64);
   } else {
     return hipErrorInvalidValue;
   }
+#undef ATW_PREFILL
   return hipGetLastError();
 }
 
