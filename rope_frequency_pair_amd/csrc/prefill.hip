@@ -52,9 +52,7 @@
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
 //  * head_dim 64 asks for four waves per SIMD (two workgroups per CU: 64 KB
-//    of LDS and at most 128 registers each); its full k-steps read their
-//    operands per k-step and the query operand from the LDS copy, which keeps
-//    the hot path free of register spills at that budget.
+//    of LDS and at most 128 registers each).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -428,12 +426,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       {
         constexpr int HALF = C::NKS / 2;
         bf16x8 ka[C::NKS][2];
-        if constexpr (D != 64) {
 #pragma unroll
-          for (int ks = C::NKS - 1; ks >= HALF; --ks) {
-            ka[ks][0] = kop(ks, 0);
-            ka[ks][1] = kop(ks, 1);
-          }
+        for (int ks = C::NKS - 1; ks >= HALF; --ks) {
+          ka[ks][0] = kop(ks, 0);
+          ka[ks][1] = kop(ks, 1);
         }
         // query operand of k-step pp's pair alone (one-hot pair slot)
         auto pair_op = [&](int pp) -> bf16x8 {
@@ -476,30 +472,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
             sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
           }
         }
-        if constexpr (D == 64) {
-          // head_dim 64: operands read per k-step, query operand from the LDS
-          // copy, so that two workgroups fit on a CU (registers)
 #pragma unroll
-          for (int ks = C::NKS - 1; ks >= 1; --ks) {
-            if (ks <= kk0) break;
-            const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qw_lds + blk_off(ks, lane));
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(ks, 0), qb, sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(ks, 1), qb, sacc[1], 0, 0, 0);
-          }
-        } else {
+        for (int ks = C::NKS - 1; ks >= 1; --ks) {
+          if (ks <= kk0) break;
+          if (ks == HALF - 1) {
 #pragma unroll
-          for (int ks = C::NKS - 1; ks >= 1; --ks) {
-            if (ks <= kk0) break;
-            if (ks == HALF - 1) {
-  #pragma unroll
-              for (int k2 = HALF - 1; k2 >= 1; --k2) {
-                ka[k2][0] = kop(k2, 0);
-                ka[k2][1] = kop(k2, 1);
-              }
+            for (int k2 = HALF - 1; k2 >= 1; --k2) {
+              ka[k2][0] = kop(k2, 0);
+              ka[k2][1] = kop(k2, 1);
             }
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
           }
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
         }
       }
       // head_dim 128: partially windowed pairs [r_any, r_full) one pair per
