@@ -412,10 +412,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
         return *reinterpret_cast<const bf16x8*>(kt + blk_off(2 * ks + blk, lane));
       };
 
-      // pairs kept for every cell: k-steps kk0..NKS-1.  k-step kk0 first,
-      // from zero, with its query operand read from the LDS copy and the
-      // pairs below r_full (partial) masked out; then the k-steps above it
-      // from the registers, from the top.  The K' operands of the upper half
+      // pairs kept for every cell: k-steps kk0..NKS-1.  k-step kk0 first
+      // (from zero; head_dim 64: on top of the partial pairs), with its
+      // query operand read from the LDS copy and the pairs below r_full
+      // (partial) masked out; then the k-steps above it with the query
+      // operands from the registers, from the top.  The K' operands of the upper half
       // of the k-steps are read before the branches (a block of a pruned
       // k-step holds stale data that is never used), the lower half once the
       // loop reaches it, so each MFMA waits only for its own reads.
