@@ -93,6 +93,14 @@ extern "C" {
  * Every resulting theta_r must be finite, > 0 and non-increasing in r (then
  * the windows grow with r and the kept pairs at any distance are a suffix);
  * otherwise the call returns ATW_EINVAL.
+ *
+ * widths (optional, any kind): when non-NULL, d/2 integer windows W_r (host
+ * memory, read during the call only) used in place of floor(k * 2*pi /
+ * theta_r); k_turns is then not used.  The rotation still uses theta_r.  Each
+ * W_r must be >= 0 and non-decreasing in r (ATW_EINVAL otherwise); values
+ * above ATW_UNBOUNDED mean unbounded.  With the window off every pair is kept
+ * as usual.  This is for windows tuned or stored per model rather than
+ * derived from k.
  */
 #define ATW_ROPE_PLAIN 0
 #define ATW_ROPE_LINEAR 1
@@ -108,6 +116,7 @@ typedef struct atw_rope {
   double high_freq_factor;      /* LLAMA3: > low_freq_factor */
   double original_max_position; /* LLAMA3: > 0 */
   const double* theta;          /* TABLE: d/2 frequencies (host) */
+  const int64_t* widths;        /* optional: d/2 explicit windows W_r (host), or NULL */
 } atw_rope;
 
 /* theta_r of every pair of a descriptor (d/2 values, host) -- host only. */

@@ -33,6 +33,12 @@ the rule in the style of a model config:
   between the blend (1 - s) theta_r/f + s theta_r, s = (L/lambda_r - a)/(b - a);
 * ``{"rope_type": "table", "theta": [...]}``: theta_r given per pair.
 
+Any of these may also carry ``"widths": [W_0, ...]``: integer windows given
+per pair that stand in for floor(k * lambda_r) (k is then unused); a dict
+with only ``"widths"`` keeps the plain frequencies.  The pages build the
+windows from the model config; a stored table is this library's extension,
+read as "pair r is kept iff the distance is at most the given W_r".
+
 "Porting to something else" asks for the retained prefix per key tile; here a
 tile plan gives, per (query tile, key tile), the first pair needed by some
 visible cell (``r_any``) and the first pair needed by every visible cell
@@ -59,9 +65,9 @@ def pair_frequencies(head_dim, rope_base, scaling=None):
         return theta
     r = np.arange(h, dtype=np.float64)
     theta = np.power(np.float64(rope_base), -2.0 * r / head_dim)
-    if scaling is None:
+    kind = None if scaling is None else scaling.get("rope_type", scaling.get("type"))
+    if kind is None or kind == "default":
         return theta
-    kind = scaling.get("rope_type", scaling.get("type"))
     if kind == "linear":
         return theta / np.float64(scaling["factor"])
     if kind == "llama3":
@@ -90,12 +96,22 @@ def pair_wavelengths(head_dim, rope_base, scaling=None):
 
 
 def window_widths(head_dim, rope_base, k_turns, window_on=True, scaling=None):
-    """Integer windows W_r = floor(k * lambda_r) as int64 (UNBOUNDED when off).
+    """Integer windows W_r = floor(k * lambda_r) as int64 (UNBOUNDED when off;
+    the explicit table when ``scaling`` holds "widths").
 
     Pair r's term is kept at integer distance delta iff delta <= W_r.
     """
     h = head_dim // 2
-    if not window_on or math.isinf(k_turns):
+    if not window_on:
+        return np.full(h, UNBOUNDED, dtype=np.int64)
+    if scaling is not None and scaling.get("widths") is not None:
+        given = [int(x) for x in scaling["widths"]]
+        if len(given) != h:
+            raise ValueError("an explicit window table needs head_dim/2 entries")
+        if min(given) < 0:
+            raise ValueError("explicit windows must be >= 0")
+        return np.array([min(x, UNBOUNDED) for x in given], dtype=np.int64)
+    if math.isinf(k_turns):
         return np.full(h, UNBOUNDED, dtype=np.int64)
     if not k_turns > 0:
         raise ValueError("k_turns must be > 0 when the window is on")

@@ -36,23 +36,34 @@ class Rope(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("base", ctypes.c_double),
                 ("factor", ctypes.c_double), ("low_freq_factor", ctypes.c_double),
                 ("high_freq_factor", ctypes.c_double), ("original_max_position", ctypes.c_double),
-                ("theta", ctypes.POINTER(ctypes.c_double))]
+                ("theta", ctypes.POINTER(ctypes.c_double)), ("widths", ctypes.POINTER(ctypes.c_int64))]
 
 
-def rope_descriptor(rope_base, rope_scaling):
+def rope_descriptor(rope_base, rope_scaling, head_dim):
     """atw_rope for a model's RoPE: rope_scaling None (plain) or a dict in the
     style of a model config: {"rope_type": "linear", "factor": f},
     {"rope_type": "llama3", "factor", "low_freq_factor", "high_freq_factor",
     "original_max_position_embeddings"}, or {"rope_type": "table", "theta":
     [theta_0, ...]} (explicit per-pair frequencies).  "type" is accepted for
-    "rope_type"."""
+    "rope_type".  Any of these may carry "widths": [W_0, ...], explicit
+    integer windows used in place of floor(k * lambda_r) (a dict with only
+    "widths" keeps the plain frequencies)."""
     r = Rope()
     r.base = float(rope_base) if rope_base is not None else 0.0
     if rope_scaling is None:
         r.kind = ATW_ROPE_PLAIN
         return r
+    if rope_scaling.get("widths") is not None:
+        wv = [int(x) for x in rope_scaling["widths"]]
+        if len(wv) != head_dim // 2:
+            raise ValueError(f"widths needs head_dim/2 = {head_dim // 2} entries (got {len(wv)})")
+        wbuf = (ctypes.c_int64 * len(wv))(*wv)
+        r.widths = ctypes.cast(wbuf, ctypes.POINTER(ctypes.c_int64))
+        r._keep_widths = wbuf
     kind = rope_scaling.get("rope_type", rope_scaling.get("type"))
-    if kind == "linear":
+    if kind is None or kind == "default":
+        r.kind = ATW_ROPE_PLAIN
+    elif kind == "linear":
         r.kind = ATW_ROPE_LINEAR
         r.factor = float(rope_scaling["factor"])
     elif kind == "llama3":
@@ -64,6 +75,8 @@ def rope_descriptor(rope_base, rope_scaling):
                                                          rope_scaling.get("original_max_position")))
     elif kind == "table":
         vals = [float(x) for x in rope_scaling["theta"]]
+        if len(vals) != head_dim // 2:
+            raise ValueError(f"theta needs head_dim/2 = {head_dim // 2} entries (got {len(vals)})")
         buf = (ctypes.c_double * len(vals))(*vals)
         r.kind = ATW_ROPE_TABLE
         r.theta = ctypes.cast(buf, ctypes.POINTER(ctypes.c_double))
@@ -204,7 +217,7 @@ def window_widths(head_dim, rope_base, k_turns, window_on=True, rope_scaling=Non
     if rope_scaling is None:
         _check(lib.atw_window_widths(head_dim, float(rope_base), float(k_turns), int(window_on), out))
     else:
-        r = rope_descriptor(rope_base, rope_scaling)
+        r = rope_descriptor(rope_base, rope_scaling, head_dim)
         _check(lib.atw_window_widths_rope(ctypes.byref(r), head_dim, float(k_turns), int(window_on), out))
     return list(out)
 
@@ -213,7 +226,7 @@ def rope_theta(head_dim, rope_base, rope_scaling=None):
     """theta_r of every pair (list of float) as the library computes them."""
     lib = load_library()
     out = (ctypes.c_double * (head_dim // 2))()
-    r = rope_descriptor(rope_base, rope_scaling)
+    r = rope_descriptor(rope_base, rope_scaling, head_dim)
     _check(lib.atw_rope_theta(ctypes.byref(r), head_dim, out))
     return list(out)
 
@@ -227,7 +240,7 @@ def pruned_terms(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, causal=True, w
         _check(lib.atw_pruned_terms(n_q, n_kv, q_pos0, head_dim, float(rope_base), float(k_turns),
                                     int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
     else:
-        r = rope_descriptor(rope_base, rope_scaling)
+        r = rope_descriptor(rope_base, rope_scaling, head_dim)
         _check(lib.atw_pruned_terms_rope(n_q, n_kv, q_pos0, head_dim, ctypes.byref(r), float(k_turns),
                                          int(causal), int(window_on), ctypes.byref(p), ctypes.byref(t)))
     return p.value, t.value
@@ -264,7 +277,7 @@ def pruned_terms_sparse(n_q, n_kv, q_pos0, head_dim, rope_base, k_turns, block_m
     m = np.ascontiguousarray(block_mask.cpu().numpy().astype(np.int32).view(np.uint32))
     if m.shape != (-(-n_q // SPARSE_BLOCK), block_mask_words(n_kv)):
         raise ValueError("block_mask must be [ceil(n_q/64), block_mask_words(n_kv)]")
-    r = rope_descriptor(rope_base, rope_scaling)
+    r = rope_descriptor(rope_base, rope_scaling, head_dim)
     p, t = ctypes.c_int64(), ctypes.c_int64()
     _check(lib.atw_pruned_terms_sparse(n_q, n_kv, q_pos0, head_dim, ctypes.byref(r), float(k_turns),
                                        int(causal), int(window_on), m.ctypes.data_as(ctypes.c_void_p),
@@ -328,7 +341,7 @@ def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=Tru
     if rope_scaling is None:
         entry, rope_arg = lib.atw_prefill, float(rope_base)
     else:
-        rdesc = rope_descriptor(rope_base, rope_scaling)
+        rdesc = rope_descriptor(rope_base, rope_scaling, D)
         entry, rope_arg = lib.atw_prefill_rope, ctypes.byref(rdesc)
     _check(entry(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
@@ -363,7 +376,7 @@ def prefill_sparse(q, k, v, block_mask, *, rope_base, k_turns, q_pos0=0, causal=
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rdesc = rope_descriptor(rope_base, rope_scaling)
+    rdesc = rope_descriptor(rope_base, rope_scaling, D)
     _check(lib.atw_prefill_sparse(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
@@ -439,7 +452,7 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
     if rope_scaling is None:
         rope_arg = float(rope_base)
     else:
-        rdesc = rope_descriptor(rope_base, rope_scaling)
+        rdesc = rope_descriptor(rope_base, rope_scaling, D)
         entry, rope_arg = entry + "_rope", ctypes.byref(rdesc)
     _check(getattr(lib, entry)(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
@@ -474,7 +487,7 @@ def decode_sparse(q, k_cache, v_cache, kv_len, q_pos, block_mask, *, rope_base, 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
     q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
-    rdesc = rope_descriptor(rope_base, rope_scaling)
+    rdesc = rope_descriptor(rope_base, rope_scaling, D)
     _check(lib.atw_decode_sparse(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
         ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
@@ -505,7 +518,7 @@ def decode_multi(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, wind
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
     q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
-    rdesc = rope_descriptor(rope_base, rope_scaling)
+    rdesc = rope_descriptor(rope_base, rope_scaling, D)
     qs = (q.stride(0), q.stride(2), q.stride(1))
     os_ = (out.stride(0), out.stride(2), out.stride(1))
     _check(lib.atw_decode_multi(

@@ -46,13 +46,21 @@ int check_window(int32_t head_dim, double rope_base, double k_turns, int32_t win
   return ATW_OK;
 }
 
-// Frequencies theta_r of a RoPE descriptor, after the head_dim / k checks.
+// Frequencies and integer windows of a RoPE descriptor.
+struct RopeWindow {
+  double theta[atw::kMaxHeadDim / 2];
+  int64_t widths[atw::kMaxHeadDim / 2];
+};
+
+// theta_r of the descriptor, then W_r: the caller's table when it gives one
+// (k is then not used), else floor(k * 2*pi / theta_r); every W_r is
+// ATW_UNBOUNDED when the window is off.
 int resolve_rope(const atw_rope* rope, int32_t head_dim, double k_turns, int32_t window_on,
-                 int max_dim, double* theta) {
+                 int max_dim, RopeWindow* out) {
   if (rope == nullptr) return fail(ATW_EINVAL, "rope is NULL");
   if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > max_dim)
     return fail(ATW_EINVAL, "head_dim must be even and in 2..%d (got %d)", max_dim, head_dim);
-  if (window_on && !(k_turns > 0.0))
+  if (window_on && rope->widths == nullptr && !(k_turns > 0.0))
     return fail(ATW_EINVAL, "k_turns must be > 0 when the window is on (got %g)", k_turns);
   atw::RopeSpec spec;
   spec.kind = rope->kind;
@@ -63,7 +71,13 @@ int resolve_rope(const atw_rope* rope, int32_t head_dim, double k_turns, int32_t
   spec.original_max_position = rope->original_max_position;
   spec.theta = rope->theta;
   const char* why = "";
-  if (!atw::rope_theta(spec, head_dim, theta, &why)) return fail(ATW_EINVAL, "rope: %s", why);
+  if (!atw::rope_theta(spec, head_dim, out->theta, &why)) return fail(ATW_EINVAL, "rope: %s", why);
+  if (rope->widths != nullptr) {
+    if (!atw::explicit_widths(head_dim / 2, rope->widths, window_on != 0, out->widths, &why))
+      return fail(ATW_EINVAL, "rope: %s", why);
+  } else {
+    atw::window_widths_theta(head_dim / 2, out->theta, k_turns, window_on != 0, out->widths);
+  }
   return ATW_OK;
 }
 
@@ -74,16 +88,14 @@ atw_rope plain_rope(double base) {
   return r;
 }
 
-// Kernel view of the window from given frequencies: W_r clamped to INT32_MAX
-// and turns per position theta_r / (2*pi).
-void fill_window_theta(atw::WindowArgs* w, int head_dim, const double* theta, double k_turns, bool on) {
-  int64_t widths[atw::kMaxHeadDim / 2];
-  atw::window_widths_theta(head_dim / 2, theta, k_turns, on, widths);
+// Kernel view of a resolved window: W_r clamped to INT32_MAX and turns per
+// position theta_r / (2*pi).
+void fill_window_rope(atw::WindowArgs* w, int head_dim, const RopeWindow& rw) {
   const double two_pi = 2.0 * 3.141592653589793;
   for (int r = 0; r < atw::kMaxPairs; ++r) {
     if (r < head_dim / 2) {
-      w->w[r] = widths[r] > (int64_t)atw::kWindowInf ? atw::kWindowInf : (int32_t)widths[r];
-      w->phi[r] = theta[r] / two_pi;
+      w->w[r] = rw.widths[r] > (int64_t)atw::kWindowInf ? atw::kWindowInf : (int32_t)rw.widths[r];
+      w->phi[r] = rw.theta[r] / two_pi;
     } else {
       w->w[r] = atw::kWindowInf;
       w->phi[r] = 0.0;
@@ -174,18 +186,18 @@ int atw_pruned_terms(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t head_dim
 
 int atw_rope_theta(const atw_rope* rope, int32_t head_dim, double* theta_out) {
   if (theta_out == nullptr) return fail(ATW_EINVAL, "theta_out is NULL");
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, 1.0, 0, atw::kMaxHeadDim, theta)) return e;
-  for (int r = 0; r < head_dim / 2; ++r) theta_out[r] = theta[r];
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, 1.0, 0, atw::kMaxHeadDim, &rw)) return e;
+  for (int r = 0; r < head_dim / 2; ++r) theta_out[r] = rw.theta[r];
   return ok();
 }
 
 int atw_window_widths_rope(const atw_rope* rope, int32_t head_dim, double k_turns,
                            int32_t window_on, int64_t* widths_out) {
   if (widths_out == nullptr) return fail(ATW_EINVAL, "widths_out is NULL");
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, widths_out);
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
+  for (int r = 0; r < head_dim / 2; ++r) widths_out[r] = rw.widths[r];
   return ok();
 }
 
@@ -196,10 +208,9 @@ int atw_pruned_terms_rope(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t hea
   if (n_q < 0 || n_kv < 0 || q_pos0 < 0) return fail(ATW_EINVAL, "n_q, n_kv, q_pos0 must be >= 0");
   if (n_q > (int64_t(1) << 40) || n_kv > (int64_t(1) << 40) || q_pos0 > (int64_t(1) << 40))
     return fail(ATW_EINVAL, "sizes above 2^40 are not supported");
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  int64_t w[atw::kMaxHeadDim / 2];
-  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, w);
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
+  const int64_t* w = rw.widths;
   atw::pruned_terms(n_q, n_kv, q_pos0, head_dim, w, causal != 0, pruned, total);
   return ok();
 }
@@ -252,7 +263,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
                  int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h_q, int32_t h_kv,
                  const int32_t* kv_head_of_q, int32_t head_dim, const int64_t* q_strides,
                  const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
-                 const double* theta, double k_turns, int32_t causal, int32_t window_on,
+                 const RopeWindow& rw, int32_t causal, int32_t window_on,
                  double softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
                  const uint32_t* block_mask = nullptr, bool sparse = false) {
   if (head_dim != 64 && head_dim != 128)
@@ -316,7 +327,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
       if (kvh[h] == kv) p.qh_of_kv[n++] = (int16_t)h;
   }
   p.kv_first[h_kv] = (int16_t)n;
-  fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
+  fill_window_rope(&p.win, head_dim, rw);
   if (sparse) {
     p.sel = block_mask;
     p.n_sel_qb = (int32_t)((n_q + atw::kSparseBlock - 1) / atw::kSparseBlock);
@@ -358,10 +369,10 @@ int atw_prefill(const void* q, const void* k, const void* v, void* o, int32_t dt
                 double softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   const atw_rope rope = plain_rope(rope_base);
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
-                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      q_strides, k_strides, v_strides, o_strides, rw, causal, window_on,
                       softmax_scale, workspace, workspace_bytes, stream);
 }
 
@@ -372,10 +383,10 @@ int atw_prefill_rope(const void* q, const void* k, const void* v, void* o, int32
                      const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
                      int32_t window_on, double softmax_scale, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
-                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      q_strides, k_strides, v_strides, o_strides, rw, causal, window_on,
                       softmax_scale, workspace, workspace_bytes, stream);
 }
 
@@ -386,10 +397,10 @@ int atw_prefill_sparse(const void* q, const void* k, const void* v, void* o, int
                        const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
                        int32_t window_on, double softmax_scale, const uint32_t* block_mask,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return prefill_impl(q, k, v, o, dtype, batch, n_q, n_kv, q_pos0, h_q, h_kv, kv_head_of_q, head_dim,
-                      q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal, window_on,
+                      q_strides, k_strides, v_strides, o_strides, rw, causal, window_on,
                       softmax_scale, workspace, workspace_bytes, stream, block_mask, true);
 }
 
@@ -407,10 +418,9 @@ int atw_pruned_terms_sparse(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h
   if (n_q > (int64_t(1) << 40) || n_kv > (int64_t(1) << 40) || q_pos0 > (int64_t(1) << 40))
     return fail(ATW_EINVAL, "sizes above 2^40 are not supported");
   if (block_mask == nullptr && n_q > 0 && n_kv > 0) return fail(ATW_EINVAL, "block_mask is NULL");
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
-  int64_t w[atw::kMaxHeadDim / 2];
-  atw::window_widths_theta(head_dim / 2, theta, k_turns, window_on != 0, w);
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
+  const int64_t* w = rw.widths;
   if (n_q == 0 || n_kv == 0) {
     *pruned = 0;
     *total = 0;
@@ -440,7 +450,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
                 const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
                 int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
                 const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
-                const int64_t* o_strides, const double* theta, double k_turns, int32_t causal,
+                const int64_t* o_strides, const RopeWindow& rw, int32_t causal,
                 int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
                 size_t workspace_bytes, void* stream, bool banded, const uint32_t* block_mask = nullptr,
                 int64_t mask_words = 0, bool sparse = false) {
@@ -535,7 +545,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
     p.sel = block_mask;
     p.sel_words = (int32_t)mask_words;
   }
-  fill_window_theta(&p.win, head_dim, theta, k_turns, window_on != 0);
+  fill_window_rope(&p.win, head_dim, rw);
   return hip_status(atw::launch_decode(p, head_dim, banded, (hipStream_t)stream), "decode launch");
 }
 
@@ -550,10 +560,10 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                size_t workspace_bytes, void* stream) {
   if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   const atw_rope rope = plain_rope(rope_base);
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rw,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, false);
 }
@@ -565,10 +575,10 @@ int atw_decode_rope(const void* q, const void* k_cache, const void* v_cache, voi
                     const int64_t* o_strides, const atw_rope* rope, double k_turns, int32_t causal,
                     int32_t window_on, double softmax_scale, int32_t num_splits, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rw,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, false);
 }
@@ -582,10 +592,10 @@ int atw_decode_banded(const void* q, const void* k_bands, const void* v_cache, v
                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (int e = check_window(head_dim, rope_base, k_turns, window_on, atw::kMaxHeadDim)) return e;
   const atw_rope rope = plain_rope(rope_base);
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(&rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return decode_impl(q, k_bands, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rw,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
 }
@@ -599,10 +609,10 @@ int atw_decode_banded_rope(const void* q, const void* k_bands, const void* v_cac
                            int32_t causal, int32_t window_on, double softmax_scale,
                            int32_t num_splits, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return decode_impl(q, k_bands, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rw,
                      causal, window_on, softmax_scale, num_splits, workspace, workspace_bytes,
                      stream, true);
 }
@@ -615,10 +625,10 @@ int atw_decode_sparse(const void* q, const void* k_cache, const void* v_cache, v
                       int32_t window_on, double softmax_scale, int32_t num_splits,
                       const uint32_t* block_mask, int64_t mask_words, int32_t k_banded,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   return decode_impl(q, k_cache, v_cache, o, dtype, batch, 1, 0, 0, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
-                     head_dim, q_strides, k_strides, v_strides, o_strides, theta, k_turns, causal,
+                     head_dim, q_strides, k_strides, v_strides, o_strides, rw, causal,
                      window_on, softmax_scale, num_splits, workspace, workspace_bytes, stream,
                      k_banded != 0, block_mask, mask_words, true);
 }
@@ -636,8 +646,8 @@ int atw_decode_multi(const void* q, const void* k_cache, const void* v_cache, vo
                      const int64_t* o_strides, int32_t k_banded, const atw_rope* rope,
                      double k_turns, int32_t window_on, double softmax_scale, int32_t num_splits,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  double theta[atw::kMaxHeadDim / 2];
-  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, theta)) return e;
+  RopeWindow rw;
+  if (int e = resolve_rope(rope, head_dim, k_turns, window_on, atw::kMaxHeadDim, &rw)) return e;
   if (q_len < 1 || q_len > 16) return fail(ATW_EINVAL, "q_len must be in 1..16 (got %d)", q_len);
   if (q_strides == nullptr || o_strides == nullptr) return fail(ATW_EINVAL, "q_strides / o_strides is NULL");
   if (q_strides[2] < 0 || o_strides[2] < 0 || (q_strides[2] * 2) % 16 != 0)
@@ -680,7 +690,7 @@ int atw_decode_multi(const void* q, const void* k_cache, const void* v_cache, vo
     void* og = static_cast<char*>(o) + (int64_t)t0 * o_strides[2] * 2;
     if (int e = decode_impl(qg, k_cache, v_cache, og, dtype, batch, n, q_strides[2], o_strides[2], kvl,
                             pos, h_q, h_kv, kv_head_of_q, head_dim, q_strides, k_strides, v_strides,
-                            o_strides, theta, k_turns, 1, window_on, softmax_scale, num_splits,
+                            o_strides, rw, 1, window_on, softmax_scale, num_splits,
                             workspace, workspace_bytes, stream, k_banded != 0))
       return e;
   }

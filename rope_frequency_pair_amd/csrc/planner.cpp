@@ -93,6 +93,21 @@ void window_widths_theta(int h, const double* theta, double k_turns, bool window
   }
 }
 
+bool explicit_widths(int h, const int64_t* table, bool window_on, int64_t* w, const char** why) {
+  for (int r = 0; r < h; ++r) {
+    if (table[r] < 0) {
+      *why = "every explicit window must be >= 0";
+      return false;
+    }
+    if (r > 0 && table[r] < table[r - 1]) {
+      *why = "explicit windows must be non-decreasing in the pair index";
+      return false;
+    }
+  }
+  for (int r = 0; r < h; ++r) w[r] = (!window_on || table[r] > kUnbounded) ? kUnbounded : table[r];
+  return true;
+}
+
 int first_retained_pair(const int64_t* w, int h, int64_t delta) {
   // w is sorted; count of entries < delta
   return static_cast<int>(std::lower_bound(w, w + h, delta) - w);

@@ -50,6 +50,11 @@ bool rope_theta(const RopeSpec& spec, int head_dim, double* theta, const char** 
 // window_widths, which it reproduces bit for bit for the plain frequencies).
 void window_widths_theta(int h, const double* theta, double k_turns, bool window_on, int64_t* w);
 
+// W_r from a caller's table: each entry >= 0 and non-decreasing in r
+// (entries above kUnbounded are taken as kUnbounded); every W_r is kUnbounded
+// when the window is off.  Returns false, with a reason, for a bad table.
+bool explicit_widths(int h, const int64_t* table, bool window_on, int64_t* w, const char** why);
+
 // Number of pairs whose window is shorter than delta (pairs pruned at that
 // distance).  w is non-decreasing; h entries.
 int first_retained_pair(const int64_t* w, int h, int64_t delta);

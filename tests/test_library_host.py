@@ -10,6 +10,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import rope_frequency_pair_amd as atw
@@ -229,6 +230,62 @@ def test_rope_scaling_rejected(lib, bad):
     assert e.value.code == binding.ATW_EINVAL
 
 
+def _explicit(d, seed):
+    """A non-decreasing window table with zeros, short windows and unbounded
+    pairs, not of the form floor(k * lambda_r)."""
+    rng = np.random.default_rng(seed)
+    h = d // 2
+    w = np.sort(rng.integers(0, 5000, h))
+    w[: h // 8] = 0
+    w[h - h // 8:] = 1 << 62
+    return [int(x) for x in w]
+
+
+@pytest.mark.parametrize("kind", [None, "llama3", "linear"])
+def test_explicit_widths_used_as_given(lib, kind):
+    for d in (64, 128):
+        table = _explicit(d, d)
+        sc = {"widths": table}
+        if kind == "llama3":
+            sc = dict(LLAMA32, widths=table)
+        elif kind == "linear":
+            sc = {"rope_type": "linear", "factor": 4.0, "widths": table}
+        for k in (8.0, 0.0, -1.0):       # k is not used with a table
+            assert atw.window_widths(d, 5e5, k, True, sc) == table
+            assert atw.window_widths(d, 5e5, k, True, sc) == list(oracle.window_widths(d, 5e5, k, True, sc))
+        # the frequencies (the rotation) are still the descriptor's
+        assert atw.rope_theta(d, 5e5, sc) == atw.rope_theta(d, 5e5, None if kind is None else
+                                                               {kk: vv for kk, vv in sc.items() if kk != "widths"})
+        assert atw.window_widths(d, 5e5, 8.0, False, sc) == [1 << 62] * (d // 2)
+        for n, q0 in ((1000, 0), (4097, 123), (131072, 0)):
+            for causal in (True, False):
+                assert atw.pruned_terms(n, n + q0, q0, d, 5e5, 1.0, causal, True, sc) == \
+                    oracle.pruned_terms(n, n + q0, q0, d, 5e5, 1.0, causal, True, sc)
+
+
+def test_explicit_widths_clamped_and_counts_sparse(lib):
+    d = 64
+    table = [0] * 8 + [3, 3, 64, 65, 200, 1000, 4096] + [9000] * 9 + [(1 << 63) - 1] * 8
+    sc = {"widths": table}
+    assert atw.window_widths(d, 1e4, 1.0, True, sc) == [min(x, 1 << 62) for x in table]
+    rng = np.random.default_rng(5)
+    n_q, n_kv, q0 = 700, 900, 200
+    sel = rng.random((-(-n_q // 64), -(-n_kv // 64))) < 0.4
+    packed = atw.pack_block_mask(torch.from_numpy(sel))
+    got = atw.pruned_terms_sparse(n_q, n_kv, q0, d, 1e4, 1.0, packed, True, True, sc)
+    ref = oracle.pruned_terms_blocks(n_q, n_kv, q0, d, 1e4, 1.0, sel, True, True, sc)
+    assert tuple(got) == tuple(ref)
+
+
+@pytest.mark.parametrize("bad", [[0, 1, 2, -1], [5, 4, 6, 7], [0, 0, 10, 9]])
+def test_explicit_widths_rejected(lib, bad):
+    with pytest.raises(atw.AtwError) as e:
+        atw.window_widths(8, 1e4, 1.0, True, {"widths": bad})
+    assert e.value.code == binding.ATW_EINVAL
+    with pytest.raises(ValueError):
+        atw.window_widths(8, 1e4, 1.0, True, {"widths": [0, 1, 2]})     # wrong length
+
+
 def _packed_rows(sel):
     """Pack a boolean [n_qb, n_kb] block selection into uint32 words (LSB first)."""
     n_qb, n_kb = sel.shape
@@ -250,7 +307,7 @@ def test_sparse_counts_bit_exact(lib, n_q, n_kv, q_pos0, causal, d, base, k):
     assert packed.shape[1] == lib.atw_block_mask_words(n_kv)
     c64 = ctypes.c_int64
     p, t = c64(), c64()
-    r = binding.rope_descriptor(base, None)
+    r = binding.rope_descriptor(base, None, d)
     assert lib.atw_pruned_terms_sparse(n_q, n_kv, q_pos0, d, ctypes.byref(r), k, int(causal), 1,
                                        packed.ctypes.data_as(ctypes.c_void_p), ctypes.byref(p),
                                        ctypes.byref(t)) == 0
@@ -270,7 +327,7 @@ def test_sparse_counts_bit_exact(lib, n_q, n_kv, q_pos0, causal, d, base, k):
 def test_sparse_invalid_arguments(lib):
     s = binding._arr64([0, 0, 0])
     fake = ctypes.c_void_p(16)
-    r = binding.rope_descriptor(1e4, None)
+    r = binding.rope_descriptor(1e4, None, 128)
 
     def pre(dtype=1, mask=fake, d=128):
         return lib.atw_prefill_sparse(fake, fake, fake, fake, dtype, 1, 10, 10, 0, 4, 2, None, d, s, s, s,
@@ -290,7 +347,7 @@ def test_sparse_invalid_arguments(lib):
 def test_decode_sparse_invalid_arguments(lib):
     s3, s2 = binding._arr64([0, 0, 0]), binding._arr64([0, 0])
     fake = ctypes.c_void_p(16)
-    r = binding.rope_descriptor(1e4, None)
+    r = binding.rope_descriptor(1e4, None, 128)
     kv = binding._arr64([5000])
     qp = binding._arr64([4999])
 
