@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import request, synth
 from tests.gpu_util import BF16_TOL, max_err, say, sync, to_np
 
@@ -56,3 +57,34 @@ def test_request_1m_sampled():
         err = max_err(got_dec[j], ref)
         say(f"  max abs err {err:.3e}")
         assert err <= BF16_TOL
+
+
+def test_one_shot_prefill_1m_sampled():
+    """The 1M prompt of the same workload in one prefill call: the query and
+    output tensors hold 28 x 2^20 x 128 = 3.8e9 elements, past 2^31, so the
+    element offsets of the last rows need 64 bits.  Sampled rows of the first
+    and last query heads against the fp64 oracle."""
+    w = synth.WORKLOADS["qwen2.5-7b-1m-request-1m"]
+    G = w.h_q // w.h_kv
+    heads = [0, w.h_q - 1]
+    kvs = sorted({h // G for h in heads})
+    hmap = [kvs.index(h // G) for h in heads]
+    say("one-shot 1m: generating inputs")
+    q, _, k, v = synth.request_inputs(w)
+    kp, vp = k[:, :, :w.n], v[:, :, :w.n]
+    assert q.numel() > 2 ** 31
+    say("one-shot 1m: prefill")
+    out = atw.prefill(q, kp, vp, rope_base=w.rope_base, k_turns=w.k_turns, q_pos0=0)
+    sync()
+    rows = [0, 1, 65535, 65536, 524289, w.n - 1]
+    got = to_np(out[:, heads][:, :, rows])
+    del out
+    kn, vn = to_np(kp[:, kvs]), to_np(vp[:, kvs])
+    for i, pos in enumerate(rows):
+        say(f"one-shot 1m: oracle row {pos}")
+        qn = to_np(q[:, heads][:, :, pos:pos + 1])
+        ref = oracle.prefill(qn, kn[:, :, :pos + 1], vn[:, :, :pos + 1], pos, w.rope_base, w.k_turns,
+                             kv_head_of_q=hmap)[:, :, 0]
+        err = max_err(got[:, :, i], ref)
+        say(f"  max abs err {err:.3e}")
+        assert np.isfinite(got[:, :, i]).all() and err <= BF16_TOL
