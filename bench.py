@@ -139,15 +139,21 @@ def cpu_baseline(sample_rows=256):
     with mp.get_context("fork").Pool(len(args)) as pool:
         pool.map(_oracle_rows, args)
     dt = time.perf_counter() - t0
-    h = w.head_dim // 2
     import oracle
     flops = 0
     for r in rows:
         p, t = oracle.pruned_terms(1, r + 1, r, w.head_dim, w.rope_base, w.k_turns)
         flops += 2 * w.head_dim * (r + 1) + 4 * (t - p)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(args), "kind": "oracle",
+    rate = flops / dt
+    # the whole step at the sampled rate (rows sampled from the second half of
+    # the sequence, so per-row cost is proportional to the flops counted)
+    p_all, t_all = oracle.pruned_terms(w.n, w.n, 0, w.head_dim, w.rope_base, w.k_turns)
+    full = w.batch * w.h_q * (2 * w.head_dim * (w.n * (w.n + 1) // 2) + 4 * (t_all - p_all))
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": len(args), "kind": "oracle",
             "sample": f"{len(rows)} query rows (positions {rows[0]}..{rows[-1]}) of one head of the "
-                      f"128K Llama-3.2-3B-shaped prefill, window on, float64 numpy; {dt:.1f} s wall"}
+                      f"128K Llama-3.2-3B-shaped prefill, window on, float64 numpy; {dt:.1f} s wall; "
+                      f"extrapolation to the whole step ({w.h_q} heads x {w.n} rows) at this rate: "
+                      f"{full / rate / 3600:.1f} h"}
 
 
 def _oracle_rows(a):
@@ -174,7 +180,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each call runs on one device; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(each call runs on one device; prefill would shard over (batch, kv head) groups and "
+              "decode over its key splits, with no change to the kernels)", file=sys.stderr)
         sys.exit(2)
 
     import torch
