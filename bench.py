@@ -179,7 +179,7 @@ def main():
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(each call runs on one device; prefill would shard over (batch, kv head) groups and "
               "decode over its key splits, with no change to the kernels)", file=sys.stderr)
         sys.exit(2)
