@@ -166,6 +166,29 @@ def _oracle_rows(a):
     return len(rows)
 
 
+def decode_profile_run(atw, synth, torch, dev):
+    """The 512K decode step alone, for counter runs: row cache ON x2, OFF x2,
+    then banded cache ON x2, OFF x2, in that launch order."""
+    wd = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+    qd, kc, vc = synth.workload_decode_inputs(wd)
+    L = wd.n
+    ws = torch.empty(atw.decode_workspace_bytes(wd.batch, wd.h_q, wd.head_dim, wd.splits),
+                     dtype=torch.uint8, device=dev)
+    od = torch.empty((wd.batch, wd.h_q, wd.head_dim), dtype=torch.bfloat16, device=dev)
+    kw = dict(rope_base=wd.rope_base, k_turns=wd.k_turns, num_splits=wd.splits, workspace=ws, out=od)
+    for on in (True, True, False, False):
+        atw.decode(qd, kc, vc, [L] * wd.batch, [L] * wd.batch, window_on=on, **kw)
+    kb = atw.kcache_band(kc)
+    for on in (True, True, False, False):
+        atw.decode_banded(qd, kb, vc, [L] * wd.batch, [L] * wd.batch, window_on=on, **kw)
+    torch.cuda.synchronize()
+    by_on, _ = decode_bytes(atw, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base, wd.k_turns, True)
+    by_off, _ = decode_bytes(atw, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base, wd.k_turns, False)
+    by_line = decode_line_bytes_banded(atw, L, L, wd.head_dim, wd.h_kv, wd.batch, wd.rope_base, wd.k_turns)
+    print(json.dumps({"decode_profile": wd.name, "bytes_on": by_on, "bytes_off": by_off,
+                      "banded_line_bytes_on": by_line}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +198,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--on-only", action="store_true",
                     help="profiling: window-on launches of the headline prefill only (no ON/OFF rounds)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="profiling: the 512K decode step only (row and banded cache, window on then "
+                         "off, two launches each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -200,6 +226,9 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 1073741824 bytes read, 1073741824 bytes written")
         del src, dst
+    if args.decode_only:
+        decode_profile_run(atw, synth, torch, dev)
+        return
     log(f"[bench] {atw.version()} on {torch.cuda.get_device_name(0)}; inputs for {w.name}")
     q, k, v = synth.workload_prefill_inputs(w)
     out = torch.empty_like(q)

@@ -4,6 +4,8 @@
     python -m rope_frequency_pair_amd.rocprof_summary counters <run_results.db> [<db> ...]
     python -m rope_frequency_pair_amd.rocprof_summary dispatches <run_results.db> \
         [--kernel SUBSTR] [--skip N] [--first N]
+    python -m rope_frequency_pair_amd.rocprof_summary sequence <run_results.db> --kernel SUBSTR \
+        --counter NAME [--copy-bytes N]
     python -m rope_frequency_pair_amd.rocprof_summary traffic --fetch <db> --write <db> \
         --kernel prefill_kernel --copy-bytes 1073741824 --sha <kernel sha> --out <json>
 
@@ -12,7 +14,9 @@
 order (optionally skipping the first N of a group and keeping the next M), so
 one workload's launches can be read apart from the others';
 ``counters`` prints the mean per-dispatch value of every collected counter
-per kernel; ``traffic`` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a
+per kernel; ``sequence`` lists one counter per dispatch in dispatch order (so
+launches of one kernel with different arguments can be told apart), in bytes
+when the calibration copy's size is given; ``traffic`` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a
 kernel into bytes, scaled by what the same counters read for the plain device
 copy of ``--copy-bytes`` bytes that bench.py --copy-calibration runs first, and
 writes the JSON bench.py reads for the roofline's ``traffic`` field.
@@ -132,6 +136,50 @@ def traffic(fetch_db, write_db, kernel, copy_bytes, copy_kernel="copyBuffer"):
     }
 
 
+def sequence(db, kernel, counter, copy_bytes=None, copy_kernel="copyBuffer"):
+    """Every dispatch of the kernels whose name contains ``kernel``, in
+    dispatch order, with its value of ``counter`` (summed over instances; the
+    name ``duration`` reads a kernel-trace database's durations in ns) and,
+    given the byte size of bench.py's calibration copy, that value in bytes
+    scaled as the copy reads."""
+    con = sqlite3.connect(db)
+    per = collections.OrderedDict()
+    if counter == "duration":       # a kernel-trace database: durations in ns
+        for i, (kn, dur) in enumerate(con.execute("select name, duration from kernels order by start")):
+            per[i] = [kn, float(dur)]
+        copy_bytes = None
+    else:
+        for kn, did, cn, val in con.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection "
+                "order by dispatch_id"):
+            if cn != counter:
+                continue
+            per.setdefault(did, [kn, 0.0])
+            per[did][1] += val
+    scale = None
+    if copy_bytes:
+        copies = [v for kn, v in per.values() if copy_kernel in kn]
+        scale = copy_bytes / copies[0] if copies and copies[0] else None
+    out = []
+    for did, (kn, v) in per.items():
+        if kernel in kn:
+            out.append({"dispatch": did, "name": kn, "value": v,
+                        "bytes": v * scale if scale else None})
+    return out, scale
+
+
+def _print_sequence(db, kernel, counter, copy_bytes):
+    rows, scale = sequence(db, kernel, counter, copy_bytes)
+    print(f"{counter} per dispatch of kernels matching '{kernel}', in dispatch order, from {db}"
+          + (f"; bytes = value x {scale:.6g} (the calibration copy)" if scale else ""))
+    print()
+    print(f"| dispatch | kernel | {counter} | bytes |")
+    print("|---|---|---|---|")
+    for r in rows:
+        b = f"{r['bytes']:.6g}" if r["bytes"] is not None else "-"
+        print(f"| {r['dispatch']} | {_short(r['name'])} | {r['value']:.6g} | {b} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -144,6 +192,11 @@ def main(argv=None):
     dsp.add_argument("--first", type=int, default=None)
     c = sub.add_parser("counters")
     c.add_argument("db", nargs="+")
+    q = sub.add_parser("sequence")
+    q.add_argument("db")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--counter", required=True)
+    q.add_argument("--copy-bytes", type=int, default=None)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -159,6 +212,8 @@ def main(argv=None):
         _print_dispatches(a.db, a.kernel, a.skip, a.first)
     elif a.cmd == "counters":
         _print_counters(a.db)
+    elif a.cmd == "sequence":
+        _print_sequence(a.db, a.kernel, a.counter, a.copy_bytes)
     else:
         r = traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.copy_kernel)
         r["kernel"] = a.kernel
