@@ -290,7 +290,8 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   if (int e = check_strides("k", k_strides, 3, elem)) return e;
   if (int e = check_strides("v", v_strides, 3, elem)) return e;
   if (int e = check_strides("o", o_strides, 3, elem)) return e;
-  const int64_t n_qblk = (n_q + atw::kPrefillBlockRows - 1) / atw::kPrefillBlockRows;
+  const int64_t rows = dtype == ATW_BF16 ? atw::prefill_bf16_block_rows(head_dim) : atw::kPrefillBlockRows;
+  const int64_t n_qblk = (n_q + rows - 1) / rows;
   if (n_qblk * h_q * batch >= (int64_t(1) << 31)) return fail(ATW_EUNSUPPORTED, "grid too large");
   if (batch > 65535) return fail(ATW_EUNSUPPORTED, "batch must be <= 65535");
   const size_t need = atw_prefill_workspace_bytes(dtype, batch, h_kv, n_kv, head_dim);

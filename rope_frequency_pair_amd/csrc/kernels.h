@@ -11,9 +11,12 @@ namespace atw {
 constexpr int kMaxHeadsQ = 256;
 constexpr int kMaxDecodeBatch = 256;
 
-// Prefill: one workgroup = 256 consecutive query rows of one query head;
-// 8 waves of 32 rows; key tiles of 64.
+// Prefill: one workgroup = consecutive query rows of one query head, 32 per
+// wave; key tiles of 64.  fp32: 8 waves (256 rows).
 constexpr int kPrefillBlockRows = 256;
+// bf16 prefill: waves (32 query rows each) per workgroup by head_dim
+constexpr int prefill_bf16_waves(int head_dim) { return head_dim == 128 ? 12 : 8; }
+constexpr int prefill_bf16_block_rows(int head_dim) { return 32 * prefill_bf16_waves(head_dim); }
 constexpr int kPrefillTileK = 64;
 
 struct PrefillParams {

@@ -18,12 +18,12 @@
 //    times on the vector ALUs, which bound the loop on this GPU.  One pass
 //    over K and V (a fraction of a percent of the attention time) removes it.
 //
-//  prefill_bf16_kernel -- one workgroup = 8 waves = 256 consecutive query
-//    rows of one query head; a wave owns 32 rows; key tiles of 64 keys,
-//    double-buffered in LDS:
+//  prefill_bf16_kernel -- one workgroup = consecutive query rows of one
+//    query head, 32 per wave (head_dim 128: 12 waves, 384 rows; head_dim 64:
+//    8 waves, 256 rows); key tiles of 64 keys, double-buffered in LDS:
 //  * staging copies 1 KB blocks straight from global memory into LDS
 //    (global_load_lds_dwordx4, no registers on the way; wave w copies blocks
-//    w, w+8, ...), one tile ahead; K' blocks of k-steps that the window
+//    w, w + waves, ...), one tile ahead; K' blocks of k-steps that the window
 //    prunes for the whole workgroup are not copied;
 //  * workgroups are dispatched largest causal blocks first, and the ones
 //    resident on one XCD (workgroup i runs on XCD i mod 8) are consecutive
@@ -51,16 +51,18 @@
 //    in the loop;
 //  * lazy rescaling of the output when the running max grows by more than
 //    2^8 (the softmax result is unchanged, only fewer rescales).
-//  * head_dim 64 asks for four waves per SIMD (two workgroups per CU: 64 KB
-//    of LDS and at most 128 registers each).
+//  * head_dim 128 runs three waves per SIMD (one workgroup of 12 waves per
+//    CU: 160 KB of LDS, at most 168 registers), which hides more of each
+//    wave's dependency stalls than two; to fit the registers, its query
+//    operands are read from the per-wave LDS copy at every k-step.  head_dim
+//    64 asks for four waves per SIMD (two workgroups of 8 waves per CU: 64 KB
+//    of LDS and at most 128 registers each), query operands in registers.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace atw {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsW = 32;
 constexpr int kTK = kPrefillTileK;
 constexpr float kRescaleLog2 = 8.0f;
@@ -72,9 +74,16 @@ struct PCfg {
   static constexpr int ND = D / 32;       // 32-wide head-dim blocks of O^T
   static constexpr int KBLK = 2 * NKS;    // K' blocks per tile: (k-step, 32-key block)
   static constexpr int VBLK = 4 * ND;     // V blocks per tile: (head-dim block, 16-key group)
-  static constexpr int KPW = KBLK / kWaves;
-  static constexpr int VPW = VBLK / kWaves;
-  static_assert(KPW >= 1 && VPW >= 1, "head_dim 64 or 128");
+  // waves per workgroup: head_dim 128 runs three waves per SIMD (12 waves,
+  // 384 rows, 160 KB of LDS), head_dim 64 four (two workgroups of 8 waves)
+  static constexpr int WAVES = prefill_bf16_waves(D);
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BLOCK_ROWS = kRowsW * WAVES;
+  static constexpr int KPW = (KBLK + WAVES - 1) / WAVES;   // staging blocks per wave
+  static constexpr int VPW = (VBLK + WAVES - 1) / WAVES;
+  // head_dim 128: query operands read from the per-wave LDS copy at every
+  // k-step (keeping them in registers would leave too few for three waves)
+  static constexpr bool Q_IN_LDS = D == 128;
 };
 
 // Element offset of the 8 bf16 values lane `lane` reads from operand block
@@ -176,13 +185,13 @@ __device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, b
 }
 
 template <int D, bool SPARSE, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf16_kernel(const PrefillParams p) {
   using C = PCfg<D>;
   constexpr int H = C::H;
   constexpr int TILE = kTK * D;
   __shared__ __attribute__((aligned(16))) __bf16 lk[2][TILE];
   __shared__ __attribute__((aligned(16))) __bf16 lv[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 lq[kWaves][C::NKS * 512];
+  __shared__ __attribute__((aligned(16))) __bf16 lq[C::WAVES][C::NKS * 512];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,8 +238,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
 
   constexpr bool causal = CAUSAL;
   const int n_kv = p.n_kv;
-  const int i0 = qb * kPrefillBlockRows;
-  const int g_last = min(i0 + kPrefillBlockRows - 1, p.n_q - 1);
+  const int i0 = qb * C::BLOCK_ROWS;
+  const int g_last = min(i0 + C::BLOCK_ROWS - 1, p.n_q - 1);
   const int w_first = i0 + wave * kRowsW;
   const int w_last = min(w_first + kRowsW - 1, p.n_q - 1);
   const bool wave_rows = w_first <= w_last;
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
   // registers and in a per-wave LDS copy (read at a k-step chosen at run time)
   __bf16* qw_lds = &lq[wave][0];
   const __bf16* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
-  bf16x8 qop[C::NKS];
+  bf16x8 qop[C::Q_IN_LDS ? 1 : C::NKS];
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
     const int r0 = 8 * ks + 4 * sh;
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
       rope_sincos(npos, p.win.phi[r0 + u], &s, &c);
       packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
     }
-    qop[ks] = __builtin_bit_cast(bf16x8, packed);
+    if constexpr (!C::Q_IN_LDS) qop[ks] = __builtin_bit_cast(bf16x8, packed);
     *reinterpret_cast<u32x4*>(qw_lds + blk_off(ks, lane)) = packed;
   }
 
@@ -297,14 +306,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
     __bf16* vd = &lv[slot][0];
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
-      const int blk = wave + kWaves * i;
-      __builtin_amdgcn_global_load_lds((const void*)(vs + blk_off(blk, lane)),
-                                       (lds_void*)(vd + blk_off(blk, 0)), 16, 0, 0);
+      const int blk = wave + C::WAVES * i;
+      if (C::VBLK % C::WAVES == 0 || blk < C::VBLK)
+        __builtin_amdgcn_global_load_lds((const void*)(vs + blk_off(blk, lane)),
+                                         (lds_void*)(vd + blk_off(blk, 0)), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::KPW; ++i) {
-      const int blk = wave + kWaves * i;
-      if ((blk >> 1) >= ks0)
+      const int blk = wave + C::WAVES * i;
+      if ((C::KBLK % C::WAVES == 0 || blk < C::KBLK) && (blk >> 1) >= ks0)
         __builtin_amdgcn_global_load_lds((const void*)(ks + blk_off(blk, lane)),
                                          (lds_void*)(kd + blk_off(blk, 0)), 16, 0, 0);
     }
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
   if constexpr (SPARSE) {
     const int qb0 = i0 / kSparseBlock;
     sel_row0 = p.sel + ((int64_t)(bb * p.h_q + hq) * p.n_sel_qb + qb0) * p.sel_words;
-    n_sel_blk = min(kPrefillBlockRows / kSparseBlock, p.n_sel_qb - qb0);
+    n_sel_blk = min(C::BLOCK_ROWS / kSparseBlock, p.n_sel_qb - qb0);
     own_blk = (wave * kRowsW) / kSparseBlock;
   }
   auto next_tile = [&](int* t, bool* own) {
@@ -361,8 +371,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
   // whole workgroup is never copied, and is read only against a fully masked
   // query operand, which needs finite data), then the first tile in LDS
 #pragma unroll
-  for (int i = 0; i < 2 * TILE / (8 * kThreads); ++i)
-    reinterpret_cast<u32x4*>(&lk[0][0])[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < (2 * TILE / 8 + C::THREADS - 1) / C::THREADS; ++i)
+    if ((2 * TILE / 8) % C::THREADS == 0 || tid + C::THREADS * i < 2 * TILE / 8)
+      reinterpret_cast<u32x4*>(&lk[0][0])[tid + C::THREADS * i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   int t = -1, t_next = -1, slot = 0;
   bool own = false, own_next = false;
@@ -483,8 +494,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void prefill_bf16_kernel
               ka[k2][1] = kop(k2, 1);
             }
           }
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qop[ks], sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qop[ks], sacc[1], 0, 0, 0);
+          bf16x8 qo;
+          if constexpr (C::Q_IN_LDS)
+            qo = *reinterpret_cast<const bf16x8*>(qw_lds + blk_off(ks, lane));
+          else
+            qo = qop[ks];
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qo, sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qo, sacc[1], 0, 0, 0);
         }
       }
       // head_dim 128: partially windowed pairs [r_any, r_full) one pair per
@@ -604,8 +620,9 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int
   const int64_t blocks = (int64_t)p.n_qblk * p.h_q * p.batch;
   if (blocks <= 0) return hipSuccess;
   dim3 pgrid((unsigned)pk.n_kt, (unsigned)pk.h_kv, (unsigned)pk.batch);
-  dim3 grid((unsigned)blocks), block(kThreads);
+  dim3 grid((unsigned)blocks);
 #define ATW_PREFILL(DD)                                                                            \
+  const dim3 block(PCfg<DD>::THREADS);                                                               \
   hipLaunchKernelGGL(pack_kv_kernel<DD>, pgrid, dim3(256), 0, stream, pk);                           \
   if (p.sel) {                                                                                       \
     if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<DD, true, true>), grid, block, 0, stream, p); \
