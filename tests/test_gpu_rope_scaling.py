@@ -159,3 +159,23 @@ def test_prefill_sparse_explicit_widths():
     err = max_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert np.isfinite(to_np(out)).all() and err <= BF16_TOL
+
+
+@pytest.mark.parametrize("banded", [False, True])
+def test_decode_multi_explicit_widths(banded):
+    """Draft tokens with an explicit window table: windows that end between
+    the tokens' distances (the per-token recomputation) come from the table."""
+    d, B, T, hq, hkv, L = 128, 2, 4, 6, 2, 700
+    sc = {"widths": _explicit_widths(d, 49, 700)}
+    say(f"decode multi explicit widths banded={banded}")
+    q = torch.randn((B, T, hq, d), generator=synth.generator(50)).to(torch.bfloat16).cuda()
+    _, kc, vc = synth.decode_inputs(B, hq, hkv, L, d, torch.bfloat16, 51, device="cuda")
+    kv_len, q_pos = [700, 404], [700 - T, 404 - T]
+    kk = atw.kcache_band(kc) if banded else kc
+    out = atw.decode_multi(q, kk, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.0, num_splits=7,
+                           k_banded=banded, rope_scaling=sc)
+    sync()
+    ref = oracle.decode_multi(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.0, scaling=sc)
+    err = max_err(to_np(out), ref)
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(to_np(out)).all() and err <= BF16_TOL
