@@ -432,7 +432,8 @@ int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, i
 /* Message of the last error on the calling thread ("" if none). */
 const char* atw_last_error(void);
 
-/* Library version string. */
+/* Library version string ("atw 0.2 (gfx950)": atw_rope carries the optional
+ * widths pointer since 0.2). */
 const char* atw_version(void);
 
 #ifdef __cplusplus

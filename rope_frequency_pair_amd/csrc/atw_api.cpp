@@ -160,7 +160,7 @@ extern "C" {
 
 const char* atw_last_error(void) { return g_last_error.c_str(); }
 
-const char* atw_version(void) { return "atw 0.1 (gfx950)"; }
+const char* atw_version(void) { return "atw 0.2 (gfx950)"; }
 
 int atw_window_widths(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
                       int64_t* widths_out) {
