@@ -222,3 +222,16 @@ def test_workload_qwen_32k_sampled_rows():
 
 def test_workload_llama_128k_sampled_rows():
     _workload_rows_check("llama-3.2-3b-128k", n_rows_random=3, heads=[0, 23])
+
+
+@pytest.mark.parametrize("n_q,q_pos0", [(383, 0), (384, 0), (385, 0), (769, 200)])
+def test_workgroup_row_boundaries(n_q, q_pos0):
+    """Query counts at and around one head_dim-128 workgroup (12 waves of 32
+    rows = 384 rows; head_dim 64 uses 256), with a chunk offset in the last
+    case: the last workgroup's idle waves and rows must not disturb the rest."""
+    say(f"prefill bf16 d=128 n_q={n_q} q_pos0={q_pos0}")
+    n_kv = n_q + q_pos0
+    q, k, v = synth.prefill_inputs(1, 3, 1, n_q, n_kv, 128, torch.bfloat16, 90 + n_q, device="cuda")
+    _run_and_compare(q, k, v, 1e4, 0.5, BF16_TOL, q_pos0=q_pos0)
+    q64, k64, v64 = synth.prefill_inputs(1, 2, 1, n_q, n_kv, 64, torch.bfloat16, 91 + n_q, device="cuda")
+    _run_and_compare(q64, k64, v64, 1e4, 0.5, BF16_TOL, q_pos0=q_pos0)
