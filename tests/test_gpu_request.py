@@ -1,26 +1,27 @@
 """The whole-request workload (Qwen2.5-7B-1M shape, one layer): chunked
 causal prefill of 1,048,576 tokens in 64K chunks, then 128 decode steps that
-append to the cache, window on, through libatw; sampled outputs against the
-fp64 oracle."""
+append to the cache, window on and window off (the request is timed both
+ways), through libatw; sampled outputs against the fp64 oracle, each row also
+within a bound relative to its own magnitude (late rows are ~1e-3)."""
 
-import numpy as np
 import pytest
 
 import oracle
 import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import request, synth
-from tests.gpu_util import BF16_TOL, max_err, say, sync, to_np
+from tests.gpu_util import check_rows, say, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
 
-def test_request_1m_sampled():
+@pytest.mark.parametrize("window_on", [True, False])
+def test_request_1m_sampled(window_on):
     w = synth.WORKLOADS["qwen2.5-7b-1m-request-1m"]
     G = w.h_q // w.h_kv
     heads = [0, w.h_q - 1]                  # kv heads 0 and 3
     kvs = sorted({h // G for h in heads})
     hmap = [kvs.index(h // G) for h in heads]
-    say("request 1m: generating inputs")
+    say(f"request 1m window_on={window_on}: generating inputs")
     q, q_dec, k, v = synth.request_inputs(w)
     bufs = request.RequestBuffers(w)
     # rows checked per chunk (offsets within the chunk)
@@ -32,8 +33,8 @@ def test_request_1m_sampled():
             got_rows[c] = to_np(out[:, heads][:, :, check[c]])
             say(f"request 1m: chunk {c} done")
 
-    say("request 1m: running (window on)")
-    _, dec = request.run_request(w, q, q_dec, k, v, bufs, window_on=True, on_chunk=keep)
+    say(f"request 1m: running (window_on={window_on})")
+    _, dec = request.run_request(w, q, q_dec, k, v, bufs, window_on=window_on, on_chunk=keep)
     sync()
     steps = [0, w.decode_steps - 1]
     got_dec = to_np(dec[steps][:, :, heads])
@@ -44,19 +45,15 @@ def test_request_1m_sampled():
             say(f"request 1m: oracle prefill row {pos}")
             qn = to_np(q[:, heads][:, :, pos:pos + 1])
             ref = oracle.prefill(qn, kn[:, :, :pos + 1], vn[:, :, :pos + 1], pos, w.rope_base, w.k_turns,
-                                 kv_head_of_q=hmap)[:, :, 0]
-            err = max_err(got_rows[c][:, :, i], ref)
-            say(f"  max abs err {err:.3e}")
-            assert err <= BF16_TOL
+                                 window_on=window_on, kv_head_of_q=hmap)[:, :, 0]
+            check_rows(got_rows[c][:, :, i], ref, f"row {pos}")
     for j, s in enumerate(steps):
         pos = w.n + s
         say(f"request 1m: oracle decode step {s} (position {pos})")
         qn = to_np(q_dec[s][:, heads])
         ref = oracle.decode(qn, kn[:, :, :pos + 1], vn[:, :, :pos + 1], [pos + 1], [pos], w.rope_base,
-                            w.k_turns, kv_head_of_q=hmap)
-        err = max_err(got_dec[j], ref)
-        say(f"  max abs err {err:.3e}")
-        assert err <= BF16_TOL
+                            w.k_turns, window_on=window_on, kv_head_of_q=hmap)
+        check_rows(got_dec[j], ref, f"decode step {s}")
 
 
 def test_one_shot_prefill_1m_sampled():
@@ -85,6 +82,4 @@ def test_one_shot_prefill_1m_sampled():
         qn = to_np(q[:, heads][:, :, pos:pos + 1])
         ref = oracle.prefill(qn, kn[:, :, :pos + 1], vn[:, :, :pos + 1], pos, w.rope_base, w.k_turns,
                              kv_head_of_q=hmap)[:, :, 0]
-        err = max_err(got[:, :, i], ref)
-        say(f"  max abs err {err:.3e}")
-        assert np.isfinite(got[:, :, i]).all() and err <= BF16_TOL
+        check_rows(got[:, :, i], ref, f"row {pos}")
