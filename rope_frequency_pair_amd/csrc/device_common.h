@@ -13,6 +13,8 @@
 namespace atw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,8 +69,32 @@ __device__ __forceinline__ int wave_pairs_below(int w_lane, int64_t delta) {
   return __popcll(__ballot((int64_t)w_lane < d));
 }
 
+// Smallest / largest distance over the visible cells of query positions
+// [n_lo, n_hi] x key positions [m_lo, m_hi], all below 2^30 (every difference
+// fits in int32); false if no cell is visible.  The prefill kernels take their
+// per-tile pair ranges from this; the plan kernel runs it for every tile.
+__device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, bool causal,
+                                       int* dmin, int* dmax) {
+  if (n_hi < n_lo || m_hi < m_lo) return false;
+  if (causal) {
+    if (m_lo > n_hi) return false;
+    *dmin = max(n_lo - m_hi, 0);
+    *dmax = n_hi - m_lo;
+  } else {
+    *dmin = m_hi < n_lo ? n_lo - m_hi : (m_lo > n_hi ? m_lo - n_hi : 0);
+    *dmax = max(abs(n_hi - m_lo), abs(n_lo - m_hi));
+  }
+  return true;
+}
+
+// First k-step (8 pairs each) that some cell at distances >= dmin needs: the
+// pairs below wave_pairs_below(dmin) are pruned for every such cell.
+__device__ __forceinline__ int first_kstep(int w_lane, int dmin) {
+  return __popcll(__ballot(w_lane < dmin)) >> 3;
+}
+
 // Smallest / largest distance over the visible cells of rows [n_lo, n_hi] x
-// keys [m_lo, m_hi] (positions).  false if no cell is visible.
+// keys [m_lo, m_hi] (positions, 64-bit).  false if no cell is visible.
 __device__ __forceinline__ bool tile_distance_range(int64_t n_lo, int64_t n_hi, int64_t m_lo,
                                                     int64_t m_hi, bool causal, int64_t* dmin,
                                                     int64_t* dmax) {
@@ -148,6 +174,42 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[0] = (__bf16)lo;
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Round two floats to fp16 (round to nearest even) and pack lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a packed pair of fp16 values (v_dot2_f32_f16 with ones).
+__device__ __forceinline__ float sum_f16x2(uint32_t packed, float acc) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+}
+
+// Power-of-two range exponents for the fp16 matrix-core operands.  fp16
+// keeps 3 more mantissa bits than bf16 but stops at 65504; a tensor whose
+// largest magnitude M reaches 2^14 is stored as x * 2^-e with the smallest
+// e >= 0 that brings M * 2^-e below 2^14 (rotated keys stay below 2^14.5),
+// and 2^e is applied back exactly in fp32.  For inputs below 2^14 e = 0 and
+// the operands are plain fp16 roundings.
+__device__ __forceinline__ int range_exp_of_float(float m) {
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;
+  return ex > 13 ? ex - 13 : 0;
+}
+// Same, from the magnitude bits (sign cleared) of a bf16 value.
+__device__ __forceinline__ int range_exp_of_bf16(uint32_t mag) {
+  const int ex = (int)((mag >> 7) & 0xff) - 127;
+  return ex > 13 ? ex - 13 : 0;
+}
+// Largest bf16 magnitude (as bits) among the 8 values of a 16-byte chunk.
+__device__ __forceinline__ uint32_t max_mag_bf16x8(u32x4 w, uint32_t acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = max(acc, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  return acc;
 }
 
 // acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 with ones).

@@ -19,13 +19,18 @@ constexpr int prefill_bf16_waves(int head_dim) { return head_dim == 128 ? 12 : 8
 constexpr int prefill_bf16_block_rows(int head_dim) { return 32 * prefill_bf16_waves(head_dim); }
 constexpr int kPrefillTileK = 64;
 
+// Range pass of the bf16 prefill: chunks of keys per (batch, kv head) whose
+// largest |k| and |v| are recorded (2 x uint32 bf16 magnitude bits each).
+constexpr int kRangeChunks = 32;
+
 struct PrefillParams {
   const void* q;
   const void* k;
   const void* v;
   void* o;
-  const void* kp;                        // bf16: packed K' / V tiles (pack_kv_kernel)
+  const void* kp;                        // bf16: packed K' / V tiles (pack_kv_kernel), fp16
   const void* vp;
+  const uint32_t* range;                 // bf16: [batch, h_kv, kRangeChunks, 2] (range_kernel)
   int64_t qs[3], ks[3], vs[3], os[3];   // element strides (batch, head, token)
   int32_t batch, n_q, n_kv, q_pos0;
   int32_t h_q, causal, n_qblk, n_kv_heads;
@@ -69,21 +74,28 @@ struct DecodeParams {
 };
 
 // Packing of K (rotated) and V into matrix-core operand order, 64-key tiles:
-// kp/vp [batch, h_kv, n_kt, 64 * head_dim] bf16.
+// kp/vp [batch, h_kv, n_kt, 64 * head_dim] fp16 (scaled by the range
+// exponents of their (batch, kv head)).
 struct PackParams {
   const void* k;
   const void* v;
   void* kp;
   void* vp;
+  uint32_t* range;                       // [batch, h_kv, kRangeChunks, 2]
   int64_t ks[3], vs[3];
   int32_t n_kv, n_kt, h_kv, batch;
   WindowArgs win;
 };
 
-// Bytes of the packed K' + V tiles of a bf16 prefill.
-inline size_t prefill_pack_bytes(int64_t batch, int64_t h_kv, int64_t n_kv, int64_t head_dim) {
+// Workspace of a bf16 prefill: packed K' tiles, packed V tiles (each
+// prefill_tile_bytes), then the range pass's chunk maxima.
+inline size_t prefill_tile_bytes(int64_t batch, int64_t h_kv, int64_t n_kv, int64_t head_dim) {
   const int64_t n_kt = (n_kv + kPrefillTileK - 1) / kPrefillTileK;
-  return (size_t)(2 * batch * h_kv * n_kt * kPrefillTileK * head_dim * 2);
+  return (size_t)(batch * h_kv * n_kt * kPrefillTileK * head_dim * 2);
+}
+inline size_t prefill_pack_bytes(int64_t batch, int64_t h_kv, int64_t n_kv, int64_t head_dim) {
+  return 2 * prefill_tile_bytes(batch, h_kv, n_kv, head_dim) +
+         (size_t)(batch * h_kv * kRangeChunks * 2 * 4);
 }
 
 struct BandParams {

@@ -1,7 +1,9 @@
 // Tile plans and per-tile pruned-term counts computed on the GPU with the
 // same device code the attention kernels use for their per-tile pair ranges
-// (tile_distance_range, wave_pairs_below) and per-cell masks (drop_bounds,
-// hide_bounds).  "ATFlash — Per-RoPE-Wavelength Attention Windows", README,
+// (span32 -- the prefill kernels' distance range, taken whenever positions
+// are below 2^30 as in every prefill call -- else the 64-bit
+// tile_distance_range the decode kernels use; wave_pairs_below) and per-cell
+// masks (drop_bounds, hide_bounds).  "ATFlash — Per-RoPE-Wavelength Attention Windows", README,
 // "Porting to something else": the retained prefix per key tile; "The idea":
 // the pruned share is input independent.
 #include "device_common.h"
@@ -15,6 +17,7 @@ __global__ __launch_bounds__(64) void plan_kernel(const PlanParams p) {
   const int w_lane = lane < p.h ? p.win.w[lane] : kWindowInf;
   const int64_t n_tiles = p.n_qt * p.n_kt;
   const int64_t n_end = p.n_kv;
+  const bool small = p.q_pos0 + p.n_q <= (int64_t(1) << 30) && p.n_kv <= (int64_t(1) << 30);
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int64_t a = tile / p.n_kt, b = tile % p.n_kt;
     const int64_t r_lo_row = a * p.tile_q;
@@ -24,7 +27,15 @@ __global__ __launch_bounds__(64) void plan_kernel(const PlanParams p) {
     const int64_t cols = min((int64_t)p.tile_k, p.n_kv - m_lo);
     const int64_t m_hi = m_lo + cols - 1;
     int64_t dmin = 0, dmax = 0;
-    const bool any = tile_distance_range(n_lo, n_hi, m_lo, m_hi, p.causal != 0, &dmin, &dmax);
+    bool any;
+    if (small) {
+      int d0 = 0, d1 = 0;
+      any = span32((int)n_lo, (int)n_hi, (int)m_lo, (int)m_hi, p.causal != 0, &d0, &d1);
+      dmin = d0;
+      dmax = d1;
+    } else {
+      any = tile_distance_range(n_lo, n_hi, m_lo, m_hi, p.causal != 0, &dmin, &dmax);
+    }
     int r_any = -1, r_full = -1;
     if (any) {
       r_any = wave_pairs_below(w_lane, dmin);

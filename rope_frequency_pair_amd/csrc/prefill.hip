@@ -9,6 +9,10 @@
 //
 // Two kernels (designed for CDNA4, not taken from the pages):
 //
+//  range_kernel -- once per call, the largest |k| and |v| of each chunk of
+//    keys of every (batch, kv head), from which the packing and attention
+//    kernels derive the same power-of-two operand scales.
+//
 //  pack_kv_kernel -- once per call, rotates every key at its position
 //    (RoPE) and writes K' and V in the order the matrix-core operands are
 //    read: a 64-key tile is a run of 1 KB blocks, one block per (operand,
@@ -45,12 +49,23 @@
 //    the fully kept k-steps above it complete the scores;
 //  * O^T += V^T P^T with P^T taken straight from the S^T registers (V is
 //    packed in the key order that register layout produces);
+//  * operands are fp16 (v_mfma_f32_32x32x16_f16, the bf16 rate on gfx950,
+//    3 more mantissa bits than bf16): rotated queries and keys, V and the
+//    softmax weights P.  A range pass finds, per (batch, kv head), the largest
+//    |k| and |v|; where they reach 2^14 the packed K' / V are scaled by a
+//    power of two that is undone exactly in fp32 (key scale folded into the
+//    query operand, value scale into the epilogue), so any bf16 input fits;
+//    the query operand carries its own per-wave power of two the same way;
+//  * scores are kept relative to a per-row reference r, in base-2 units: the
+//    query operand holds softmax_scale * log2(e), and the first QK^T MFMA of
+//    a tile starts from -r instead of zero, so P = exp2(S) needs no per-score
+//    arithmetic.  r trails the running max by 6 (P <= 2^14 stays in fp16 and
+//    small weights stay out of its subnormals) and is raised only when a score
+//    passes it by more than 14 (lazy rescale);
 //  * one workgroup barrier per tile; tile geometry (distances, pair ranges)
 //    is wave-uniform and runs on the scalar unit; causal / non-causal and
 //    dense / block-sparse are separate instantiations, so neither is tested
 //    in the loop;
-//  * lazy rescaling of the output when the running max grows by more than
-//    2^8 (the softmax result is unchanged, only fewer rescales).
 //  * head_dim 128 runs three waves per SIMD (one workgroup of 12 waves per
 //    CU: 160 KB of LDS, at most 168 registers), which hides more of each
 //    wave's dependency stalls than two; to fit the registers, its query
@@ -65,7 +80,27 @@ namespace {
 
 constexpr int kRowsW = 32;
 constexpr int kTK = kPrefillTileK;
-constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRefLag = 6.0f;       // reference r = running max - 6 (base 2)
+constexpr float kRaise = 14.0f;       // raise r when a score passes it by more
+
+// Power-of-two scales of one (batch, kv head): the range pass's chunk maxima
+// (bf16 magnitude bits of K and V) reduced by one wave.  Wave-uniform.
+__device__ __forceinline__ void head_range_exps(const uint32_t* range, int64_t head, int* ek, int* ev) {
+  const int lane = threadIdx.x & 63;
+  uint32_t mk = 0, mv = 0;
+  if (lane < kRangeChunks) {
+    const u32x2 m = *reinterpret_cast<const u32x2*>(range + (head * kRangeChunks + lane) * 2);
+    mk = m[0];
+    mv = m[1];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+    mv = max(mv, (uint32_t)__shfl_xor((int)mv, o));
+  }
+  *ek = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(mk));
+  *ev = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(mv));
+}
 
 template <int D>
 struct PCfg {
@@ -100,6 +135,42 @@ __device__ __forceinline__ constexpr int pv_key(int g, int s, int j) {
   return 32 * (g >> 1) + 16 * (g & 1) + 8 * (j >> 2) + 4 * s + (j & 3);
 }
 
+// Largest |k| and |v| (bf16 magnitude bits) over keys [c * per, (c+1) * per)
+// of one (batch, kv head), per = ceil(n_kv / kRangeChunks).
+template <int D>
+__global__ __launch_bounds__(256) void range_kernel(const PackParams p) {
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  __shared__ uint32_t red[2][4];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int per = (p.n_kv + kRangeChunks - 1) / kRangeChunks;
+  const int m0 = min(c * per, p.n_kv), m1 = min(m0 + per, p.n_kv);
+  const __bf16* kb = (const __bf16*)p.k + b * p.ks[0] + h * p.ks[1];
+  const __bf16* vb = (const __bf16*)p.v + b * p.vs[0] + h * p.vs[1];
+  uint32_t mk = 0, mv = 0;
+  for (int i = tid; i < (m1 - m0) * CPR; i += 256) {
+    const int m = m0 + i / CPR, ch = i % CPR;
+    mk = max_mag_bf16x8(*reinterpret_cast<const u32x4*>(kb + (int64_t)m * p.ks[2] + ch * 8), mk);
+    mv = max_mag_bf16x8(*reinterpret_cast<const u32x4*>(vb + (int64_t)m * p.vs[2] + ch * 8), mv);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+    mv = max(mv, (uint32_t)__shfl_xor((int)mv, o));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = mk;
+    red[1][tid >> 6] = mv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t head = (int64_t)b * p.h_kv + h;
+    u32x2 out;
+    out[0] = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
+    out[1] = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    *reinterpret_cast<u32x2*>(p.range + (head * kRangeChunks + c) * 2) = out;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
   using C = PCfg<D>;
@@ -113,8 +184,10 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
   const __bf16* kb = (const __bf16*)p.k + b * p.ks[0] + h * p.ks[1];
   const __bf16* vb = (const __bf16*)p.v + b * p.vs[0] + h * p.vs[1];
   const int64_t tix = ((int64_t)b * p.h_kv + h) * p.n_kt + tile;
-  __bf16* kp = (__bf16*)p.kp + tix * (kTK * D);
-  __bf16* vp = (__bf16*)p.vp + tix * (kTK * D);
+  uint16_t* kp = (uint16_t*)p.kp + tix * (kTK * D);
+  uint16_t* vp = (uint16_t*)p.vp + tix * (kTK * D);
+  int ek, ev;
+  head_range_exps(p.range, (int64_t)b * p.h_kv + h, &ek, &ev);
 
   // row-major copy of the tile into LDS; keys past n_kv are zero
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -132,7 +205,8 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
   __syncthreads();
 
   // K' blocks: lane l of block (ks, blk) holds key 32*blk + l%32, pairs
-  // 8*ks + 4*(l/32) + u, u = 0..3, rotated, as (x_r, x_{r+h}) bf16 pairs
+  // 8*ks + 4*(l/32) + u, u = 0..3, rotated and scaled by 2^-ek, as
+  // (x_r, x_{r+h}) fp16 pairs
   for (int it = tid; it < C::KBLK * 64; it += 256) {
     const int blk = it >> 6, lane = it & 63;
     const int key = 32 * (blk & 1) + (lane & 31);
@@ -144,44 +218,24 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const PackParams p) {
       const float x1 = (float)sk[key][r0 + u], x2 = (float)sk[key][H + r0 + u];
       float s, c;
       rope_sincos(m, p.win.phi[r0 + u], &s, &c);
-      out[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
+      out[u] = pack_f16(__builtin_amdgcn_ldexpf(x1 * c - x2 * s, -ek),
+                        __builtin_amdgcn_ldexpf(x2 * c + x1 * s, -ek));
     }
     *reinterpret_cast<u32x4*>(kp + blk_off(blk, lane)) = out;
   }
   // V blocks: lane l of block (bd, g) holds head-dim 32*bd + l%32 of keys
-  // pv_key(g, l/32, j), j = 0..7
+  // pv_key(g, l/32, j), j = 0..7, scaled by 2^-ev, fp16
   for (int it = tid; it < C::VBLK * 64; it += 256) {
     const int blk = it >> 6, lane = it & 63;
     const int bd = blk >> 2, g = blk & 3;
     const int dim = 32 * bd + (lane & 31), s = lane >> 5;
     u32x4 out;
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      bf16x2 w;
-      w[0] = sv[pv_key(g, s, j)][dim];
-      w[1] = sv[pv_key(g, s, j + 1)][dim];
-      out[j >> 1] = __builtin_bit_cast(uint32_t, w);
-    }
+    for (int j = 0; j < 8; j += 2)
+      out[j >> 1] = pack_f16(__builtin_amdgcn_ldexpf((float)sv[pv_key(g, s, j)][dim], -ev),
+                             __builtin_amdgcn_ldexpf((float)sv[pv_key(g, s, j + 1)][dim], -ev));
     *reinterpret_cast<u32x4*>(vp + blk_off(blk, lane)) = out;
   }
-}
-
-// Smallest / largest distance over the visible cells of query positions
-// [n_lo, n_hi] x key positions [m_lo, m_hi] (all below 2^30, so every
-// difference fits in int32); false if no cell is visible.
-__device__ __forceinline__ bool span32(int n_lo, int n_hi, int m_lo, int m_hi, bool causal,
-                                       int* dmin, int* dmax) {
-  if (n_hi < n_lo || m_hi < m_lo) return false;
-  if (causal) {
-    if (m_lo > n_hi) return false;
-    *dmin = max(n_lo - m_hi, 0);
-    *dmax = n_hi - m_lo;
-  } else {
-    *dmin = m_hi < n_lo ? n_lo - m_hi : (m_lo > n_hi ? m_lo - n_hi : 0);
-    *dmax = max(abs(n_hi - m_lo), abs(n_lo - m_hi));
-  }
-  return true;
 }
 
 template <int D, bool SPARSE, bool CAUSAL>
@@ -189,9 +243,9 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   using C = PCfg<D>;
   constexpr int H = C::H;
   constexpr int TILE = kTK * D;
-  __shared__ __attribute__((aligned(16))) __bf16 lk[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 lv[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 lq[C::WAVES][C::NKS * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t lk[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t lq[C::WAVES][C::NKS * 512];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -233,8 +287,10 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   const __bf16* qbase = (const __bf16*)p.q + bb * p.qs[0] + hq * p.qs[1];
   __bf16* obase = (__bf16*)p.o + bb * p.os[0] + hq * p.os[1];
   const int64_t tix0 = ((int64_t)bb * p.n_kv_heads + kvh) * p.n_kt;
-  const __bf16* kpk = (const __bf16*)p.kp + tix0 * TILE;
-  const __bf16* vpk = (const __bf16*)p.vp + tix0 * TILE;
+  const uint16_t* kpk = (const uint16_t*)p.kp + tix0 * TILE;
+  const uint16_t* vpk = (const uint16_t*)p.vp + tix0 * TILE;
+  int ek, ev;
+  head_range_exps(p.range, (int64_t)bb * p.n_kv_heads + kvh, &ek, &ev);
 
   constexpr bool causal = CAUSAL;
   const int n_kv = p.n_kv;
@@ -249,34 +305,57 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   const int npos = p.q_pos0 + qrow;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
 
-  // ---- query: load, rotate at its position, keep as MFMA operand (lane l:
-  // query l%32, pairs 8ks + 4(l/32) + u as (x_r, x_{r+h}) pairs), in
-  // registers and in a per-wave LDS copy (read at a k-step chosen at run time)
-  __bf16* qw_lds = &lq[wave][0];
+  // ---- query: load, rotate at its position, scale by softmax_scale *
+  // log2(e) (scores in base-2 units) and by 2^ek (undoes the key scale), keep
+  // as fp16 MFMA operand (lane l: query l%32, pairs 8ks + 4(l/32) + u as
+  // (x_r, x_{r+h}) pairs), in registers and in a per-wave LDS copy (read at a
+  // k-step chosen at run time).  If the wave's largest value reaches 2^14 the
+  // operand carries 2^-eq, undone on the scores.
+  uint16_t* qw_lds = &lq[wave][0];
   const __bf16* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
-  bf16x8 qop[C::Q_IN_LDS ? 1 : C::NKS];
+  f16x8 qop[C::Q_IN_LDS ? 1 : C::NKS];
+  int eq;
+  {
+    const float cq = __builtin_amdgcn_ldexpf(p.scale_log2, ek);
+    float qt[C::NKS][8];
+    float qmax = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    const int r0 = 8 * ks + 4 * sh;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(qrow_ptr + r0);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(qrow_ptr + H + r0);
-    u32x4 packed;
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const int r0 = 8 * ks + 4 * sh;
+      const u32x2 a = *reinterpret_cast<const u32x2*>(qrow_ptr + r0);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(qrow_ptr + H + r0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
-      const float x2 = (u & 1) ? bf16_hi(b[u >> 1]) : bf16_lo(b[u >> 1]);
-      float s, c;
-      rope_sincos(npos, p.win.phi[r0 + u], &s, &c);
-      packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
+      for (int u = 0; u < 4; ++u) {
+        const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
+        const float x2 = (u & 1) ? bf16_hi(b[u >> 1]) : bf16_lo(b[u >> 1]);
+        float s, c;
+        rope_sincos(npos, p.win.phi[r0 + u], &s, &c);
+        qt[ks][2 * u] = (x1 * c - x2 * s) * cq;
+        qt[ks][2 * u + 1] = (x2 * c + x1 * s) * cq;
+        qmax = fmaxf(qmax, fmaxf(fabsf(qt[ks][2 * u]), fabsf(qt[ks][2 * u + 1])));
+      }
     }
-    if constexpr (!C::Q_IN_LDS) qop[ks] = __builtin_bit_cast(bf16x8, packed);
-    *reinterpret_cast<u32x4*>(qw_lds + blk_off(ks, lane)) = packed;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+    eq = __builtin_amdgcn_readfirstlane(range_exp_of_float(qmax));
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      u32x4 packed;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        packed[u] = pack_f16(__builtin_amdgcn_ldexpf(qt[ks][2 * u], -eq),
+                             __builtin_amdgcn_ldexpf(qt[ks][2 * u + 1], -eq));
+      if constexpr (!C::Q_IN_LDS) qop[ks] = __builtin_bit_cast(f16x8, packed);
+      *reinterpret_cast<u32x4*>(qw_lds + blk_off(ks, lane)) = packed;
+    }
   }
+  const float score_unscale = __builtin_amdgcn_ldexpf(1.0f, eq);   // scores carry 2^-eq
 
   f32x16 oacc[C::ND];
 #pragma unroll
   for (int b = 0; b < C::ND; ++b) oacc[b] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float r_ref = 0.f, l_run = 0.f;   // reference (base 2) and running sum of the weights
+  float raise_at = -INFINITY;       // kRaise once a visible key has set r_ref
 
   const int kv_end = causal ? min(n_kv, gn_hi + 1) : n_kv;
   const int n_kt = (kv_end + kTK - 1) / kTK;
@@ -295,15 +374,15 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
     int dmin = 0, dmax = 0;
     if (!span32(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return C::NKS;
-    return wave_pairs_below(w_lane, dmin) >> 3;
+    return first_kstep(w_lane, dmin);
   };
   typedef __attribute__((address_space(3))) void lds_void;
   auto dma = [&](int t, int slot) {
     const int ks0 = stage_ks(t);
-    const __bf16* ks = kpk + (int64_t)t * TILE;
-    const __bf16* vs = vpk + (int64_t)t * TILE;
-    __bf16* kd = &lk[slot][0];
-    __bf16* vd = &lv[slot][0];
+    const uint16_t* ks = kpk + (int64_t)t * TILE;
+    const uint16_t* vs = vpk + (int64_t)t * TILE;
+    uint16_t* kd = &lk[slot][0];
+    uint16_t* vd = &lv[slot][0];
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const int blk = wave + C::WAVES * i;
@@ -393,12 +472,23 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
       const int r_any = wave_pairs_below(w_lane, dmin);
       const int r_full = wave_pairs_below(w_lane, dmax);
       const int kbase_lane = m_lo + 4 * sh;
-      const __bf16* kt = &lk[slot][0];
-      const __bf16* vt = &lv[slot][0];
+      const uint16_t* kt = &lk[slot][0];
+      const uint16_t* vt = &lv[slot][0];
+      // scores start from -r (in the operand's 2^-eq units)
+      const float init = -r_ref * __builtin_amdgcn_ldexpf(1.0f, -eq);
       f32x16 sacc[2];
+      // accumulators set to -r in place, so the first MFMA of each chain
+      // reads and writes the same registers
+      auto start = [&]() {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sacc[0][v] = init;
+          sacc[1][v] = init;
+        }
+      };
 
       // reset the cells of x beyond the window of partially windowed pair pp
-      auto drop_cells = [&](f32x16 (&x)[2], int pp) {
+      auto drop_cells = [&](f32x16 (&x)[2], int pp, float reset) {
         int thr_lo, thr_hi;
         drop_bounds(npos, p.win.w[pp], kbase_lane, causal, kTK, &thr_lo, &thr_hi);
         if constexpr (CAUSAL) {
@@ -408,43 +498,47 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
           for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (32 * blk + acc_row(v) < thr_lo) x[blk][v] = 0.f;
+              if (32 * blk + acc_row(v) < thr_lo) x[blk][v] = reset;
         } else {
 #pragma unroll
           for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int ko = 32 * blk + acc_row(v);
-              if (ko < thr_lo || ko > thr_hi) x[blk][v] = 0.f;
+              if (ko < thr_lo || ko > thr_hi) x[blk][v] = reset;
             }
         }
       };
-      auto kop = [&](int ks, int blk) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(kt + blk_off(2 * ks + blk, lane));
+      auto kop = [&](int ks, int blk) -> f16x8 {
+        return *reinterpret_cast<const f16x8*>(kt + blk_off(2 * ks + blk, lane));
+      };
+      auto mfma = [](f16x8 a, f16x8 b, f32x16 c) -> f32x16 {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
       };
 
       // pairs kept for every cell: k-steps kk0..NKS-1.  k-step kk0 first
-      // (from zero; head_dim 64: on top of the partial pairs), with its
-      // query operand read from the LDS copy and the pairs below r_full
-      // (partial) masked out; then the k-steps above it with the query
-      // operands from the registers, from the top.  The K' operands of the upper half
-      // of the k-steps are read before the branches (a block of a pruned
-      // k-step holds stale data that is never used), the lower half once the
-      // loop reaches it, so each MFMA waits only for its own reads.
-      // (r_full == H, every pair partial or pruned: k-step NKS-1 with all its
-      // slots masked, which yields zero; its K' slot holds finite data, as
-      // the K' buffers start zeroed)
+      // (from -r; head_dim 64: on top of the partial pairs), with its query
+      // operand read from the LDS copy and the pairs below r_full (partial)
+      // masked out; then the k-steps above it with the query operands from
+      // the registers (head_dim 128: the LDS copy), from the top.  The K'
+      // operands of the upper half of the k-steps are read before the
+      // branches (a block of a pruned k-step holds stale data that is never
+      // used), the lower half once the loop reaches it, so each MFMA waits
+      // only for its own reads.  (r_full == H, every pair partial or pruned:
+      // k-step NKS-1 with all its slots masked, which yields -r; its K' slot
+      // holds finite data, as the K' buffers start zeroed)
       const int kk0 = min(r_full >> 3, C::NKS - 1);
       {
-        constexpr int HALF = C::NKS / 2;
-        bf16x8 ka[C::NKS][2];
+        // (head_dim 64: no early reads, its register budget is 128)
+        constexpr int HALF = D == 64 ? C::NKS : C::NKS / 2;
+        f16x8 ka[C::NKS][2];
 #pragma unroll
         for (int ks = C::NKS - 1; ks >= HALF; --ks) {
           ka[ks][0] = kop(ks, 0);
           ka[ks][1] = kop(ks, 1);
         }
         // query operand of k-step pp's pair alone (one-hot pair slot)
-        auto pair_op = [&](int pp) -> bf16x8 {
+        auto pair_op = [&](int pp) -> f16x8 {
           const int ks = pp >> 3, uu = pp & 7;
           const uint32_t qd =
               *reinterpret_cast<const uint32_t*>(qw_lds + blk_off(ks, lane) + 2 * (uu & 3));
@@ -452,81 +546,85 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
           u32x4 bw;
 #pragma unroll
           for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
-          return __builtin_bit_cast(bf16x8, bw);
+          return __builtin_bit_cast(f16x8, bw);
         };
         {
           u32x4 bw = *reinterpret_cast<const u32x4*>(qw_lds + blk_off(kk0, lane));
           const int tau = r_full - 8 * kk0 - 4 * sh;   // slots below tau are partial
 #pragma unroll
           for (int u = 0; u < 4; ++u) bw[u] = (u < tau) ? 0u : bw[u];
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+          const f16x8 bop = __builtin_bit_cast(f16x8, bw);
           if (D == 64 && r_any < r_full) {
             // partially windowed pairs [r_any, r_full) first, one pair per
             // MFMA, ascending, each followed by the reset of the cells beyond
-            // its window (windows grow with r, so what remains is exactly the
-            // kept partial terms); then the masked k-step on top
-            {
-              const bf16x8 b0 = pair_op(r_any);
-              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(r_any >> 3, 0), b0, f32x16{}, 0, 0, 0);
-              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(r_any >> 3, 1), b0, f32x16{}, 0, 0, 0);
-              drop_cells(sacc, r_any);
+            // its window to -r (windows grow with r, so what remains is
+            // exactly the kept partial terms); then the masked k-step on top
+            start();
+            for (int pp = r_any; pp < r_full; ++pp) {
+              const f16x8 bp = pair_op(pp);
+              sacc[0] = mfma(kop(pp >> 3, 0), bp, sacc[0]);
+              sacc[1] = mfma(kop(pp >> 3, 1), bp, sacc[1]);
+              drop_cells(sacc, pp, init);
             }
-            for (int pp = r_any + 1; pp < r_full; ++pp) {
-              const bf16x8 bp = pair_op(pp);
-              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(pp >> 3, 0), bp, sacc[0], 0, 0, 0);
-              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(pp >> 3, 1), bp, sacc[1], 0, 0, 0);
-              drop_cells(sacc, pp);
-            }
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, sacc[1], 0, 0, 0);
+            sacc[0] = mfma(kop(kk0, 0), bop, sacc[0]);
+            sacc[1] = mfma(kop(kk0, 1), bop, sacc[1]);
           } else {
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 0), bop, f32x16{}, 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(kk0, 1), bop, f32x16{}, 0, 0, 0);
+            start();
+            sacc[0] = mfma(kop(kk0, 0), bop, sacc[0]);
+            sacc[1] = mfma(kop(kk0, 1), bop, sacc[1]);
           }
         }
 #pragma unroll
         for (int ks = C::NKS - 1; ks >= 1; --ks) {
           if (ks <= kk0) break;
-          if (ks == HALF - 1) {
+          if (D == 64) {
+            ka[ks][0] = kop(ks, 0);
+            ka[ks][1] = kop(ks, 1);
+          } else if (ks == HALF - 1) {
 #pragma unroll
             for (int k2 = HALF - 1; k2 >= 1; --k2) {
               ka[k2][0] = kop(k2, 0);
               ka[k2][1] = kop(k2, 1);
             }
           }
-          bf16x8 qo;
+          f16x8 qo;
           if constexpr (C::Q_IN_LDS)
-            qo = *reinterpret_cast<const bf16x8*>(qw_lds + blk_off(ks, lane));
+            qo = *reinterpret_cast<const f16x8*>(qw_lds + blk_off(ks, lane));
           else
             qo = qop[ks];
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qo, sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qo, sacc[1], 0, 0, 0);
+          sacc[0] = mfma(ka[ks][0], qo, sacc[0]);
+          sacc[1] = mfma(ka[ks][1], qo, sacc[1]);
         }
       }
       // head_dim 128: partially windowed pairs [r_any, r_full) one pair per
       // MFMA into a separate accumulator, ascending, each followed by the
-      // reset, then added (head_dim 64 handled them above, before the kept
-      // k-steps, in the same accumulator: no zeroing and no final add, which
-      // matters at its budget of 128 registers and vector-bound tile; at
-      // head_dim 128 the separate accumulator measured faster)
+      // reset to zero, then added (head_dim 64 handled them above, before the
+      // kept k-steps, in the same accumulator: no zeroing and no final add,
+      // which matters at its budget of 128 registers and vector-bound tile;
+      // at head_dim 128 the separate accumulator measured faster)
       if (D != 64 && r_any < r_full) {
         f32x16 x[2] = {f32x16{}, f32x16{}};
         for (int pp = r_any; pp < r_full; ++pp) {
           const int ks = pp >> 3, uu = pp & 7;
-          const bf16x8 a0 = kop(ks, 0), a1 = kop(ks, 1);
+          const f16x8 a0 = kop(ks, 0), a1 = kop(ks, 1);
           const uint32_t qd =
               *reinterpret_cast<const uint32_t*>(qw_lds + blk_off(ks, lane) + 2 * (uu & 3));
           const bool mine = sh == (uu >> 2);
           u32x4 bw;
 #pragma unroll
           for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-          x[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, x[0], 0, 0, 0);
-          x[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, x[1], 0, 0, 0);
-          drop_cells(x, pp);
+          const f16x8 bop = __builtin_bit_cast(f16x8, bw);
+          x[0] = mfma(a0, bop, x[0]);
+          x[1] = mfma(a1, bop, x[1]);
+          drop_cells(x, pp, 0.f);
         }
         sacc[0] += x[0];
         sacc[1] += x[1];
+      }
+      // the query operand's power of two (only for queries reaching 2^14)
+      if (eq != 0) {
+        sacc[0] *= score_unscale;
+        sacc[1] *= score_unscale;
       }
 
       // causal and ragged-tail masks (cells outside the attended set)
@@ -543,46 +641,50 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
           }
       }
 
-      // online softmax (base 2, scale folded into the exponent)
+      // online softmax on scores relative to r (base 2): raise r when a score
+      // passes it by more than kRaise, or at the row's first visible key
       float mx = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[blk][v]);
       mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
-      if (__any(grow)) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * p.scale_log2);
+      const bool raise = mx > raise_at;
+      if (__any(raise)) {
+        const float dr = raise ? mx - kRefLag : 0.f;
+        // < 2^-8 where a running sum exists; a row's first raise multiplies
+        // zeros (min keeps it finite for very negative first scores)
+        const float alpha = fminf(exp2f(-dr), 1.f);
 #pragma unroll
         for (int b = 0; b < C::ND; ++b) oacc[b] *= alpha;
         l_run *= alpha;
-        m_run = m_new;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) sacc[blk] -= dr;
+        r_ref += dr;
+        raise_at = raise ? kRaise : raise_at;
       }
-      const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
       float lsum = 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // V operands of this key group first, so their LDS latency overlaps
         // the exponentials below
-        bf16x8 va[C::ND];
+        f16x8 va[C::ND];
 #pragma unroll
         for (int b = 0; b < C::ND; ++b)
-          va[b] = *reinterpret_cast<const bf16x8*>(vt + blk_off(4 * b + g, lane));
+          va[b] = *reinterpret_cast<const f16x8*>(vt + blk_off(4 * b + g, lane));
         u32x4 pw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v0 = 8 * (g & 1) + 2 * i;
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0], p.scale_log2, -mb));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0 + 1], p.scale_log2, -mb));
-          pw[i] = pack_bf16(e0, e1);
+          const float e0 = __builtin_amdgcn_exp2f(sacc[g >> 1][v0]);
+          const float e1 = __builtin_amdgcn_exp2f(sacc[g >> 1][v0 + 1]);
+          pw[i] = pack_f16(e0, e1);
           // the normalizer sums the same rounded weights the PV product uses
-          lsum = sum_bf16x2(pw[i], lsum);
+          lsum = sum_f16x2(pw[i], lsum);
         }
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+        const f16x8 pop = __builtin_bit_cast(f16x8, pw);
 #pragma unroll
-        for (int b = 0; b < C::ND; ++b)
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[b], pop, oacc[b], 0, 0, 0);
+        for (int b = 0; b < C::ND; ++b) oacc[b] = mfma(va[b], pop, oacc[b]);
       }
       l_run += lsum;
     }
@@ -594,9 +696,10 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
     slot ^= 1;
   }
 
-  // ---- epilogue: O = O^T / l
+  // ---- epilogue: O = O^T * 2^ev / l
   const float l_tot = half_swap_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // a row without an attended key gives 0
+  // a row without an attended key gives 0
+  const float inv = l_tot > 0.f ? __builtin_amdgcn_ldexpf(1.f / l_tot, ev) : 0.f;
   const int row = w_first + l32;
   if (wave_rows && row <= w_last) {
     __bf16* orow = obase + (int64_t)row * p.os[2];
@@ -620,9 +723,11 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int
   const int64_t blocks = (int64_t)p.n_qblk * p.h_q * p.batch;
   if (blocks <= 0) return hipSuccess;
   dim3 pgrid((unsigned)pk.n_kt, (unsigned)pk.h_kv, (unsigned)pk.batch);
+  dim3 rgrid((unsigned)kRangeChunks, (unsigned)pk.h_kv, (unsigned)pk.batch);
   dim3 grid((unsigned)blocks);
 #define ATW_PREFILL(DD)                                                                            \
   const dim3 block(PCfg<DD>::THREADS);                                                               \
+  hipLaunchKernelGGL(range_kernel<DD>, rgrid, dim3(256), 0, stream, pk);                             \
   hipLaunchKernelGGL(pack_kv_kernel<DD>, pgrid, dim3(256), 0, stream, pk);                           \
   if (p.sel) {                                                                                       \
     if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<DD, true, true>), grid, block, 0, stream, p); \

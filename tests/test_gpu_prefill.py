@@ -15,7 +15,8 @@ import torch
 import oracle
 import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import synth
-from tests.gpu_util import BF16_TOL, F32_TOL, max_err, sample_rows, say, sync, to_np
+from tests.gpu_util import (BF16_TOL, F32_TOL, ROW_ABS, ROW_REL, check_rows, max_err, sample_rows, say,
+                            sync, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +54,22 @@ def test_bf16_ragged_gqa(d, k_turns):
     say(f"prefill bf16 ragged d={d} k={k_turns}")
     q, k, v = synth.prefill_inputs(2, 4, 2, 700, 700, d, torch.bfloat16, 7, device="cuda")
     _run_and_compare(q, k, v, 1e4, k_turns, BF16_TOL)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("k_turns", [0.35, 4.0])
+def test_bf16_seed_sweep(d, k_turns):
+    """The ragged 700-row GQA case over 32 seeds (stops at the first failure):
+    the 1e-2 bar holds on every draw, not on a chosen one."""
+    for seed in range(1000, 1032):
+        q, k, v = synth.prefill_inputs(1, 4, 2, 700, 700, d, torch.bfloat16, seed, device="cuda")
+        out = atw.prefill(q, k, v, rope_base=1e4, k_turns=k_turns)
+        sync()
+        ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, k_turns)
+        got = to_np(out)
+        err = max_err(got, ref)
+        say(f"  seed {seed} d={d} k={k_turns}: max abs err {err:.3e}")
+        assert np.isfinite(got).all() and err <= BF16_TOL, (seed, err)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -204,16 +221,18 @@ def _workload_rows_check(name, n_rows_random=6, heads=None):
                                           w.rope_base, w.k_turns, window_on=window_on,
                                           kv_head_of_q=hmap)[:, :, 0]
         got = to_np(out[:, heads][:, :, rows])
-        err = max_err(got, ref)
-        say(f"  window_on={window_on} max abs err {err:.3e}")
-        assert err <= BF16_TOL
+        check_rows(got, ref, f"window_on={window_on}")
         if window_on:
             ref_on, got_on = ref, got
         else:
-            # the window's effect itself matches: (on - off) against the oracle's difference
+            # the window's effect itself matches: (on - off) against the
+            # oracle's difference, per row relative to the row's outputs
             diff_err = max_err(got_on - got, ref_on - ref)
-            say(f"  (on - off) max abs err {diff_err:.3e}")
+            row_err = np.abs((got_on - got) - (ref_on - ref)).max(axis=-1)
+            bound = 2 * (ROW_REL * np.maximum(np.abs(ref_on).max(axis=-1), np.abs(ref).max(axis=-1)) + ROW_ABS)
+            say(f"  (on - off) max abs err {diff_err:.3e}, worst row ratio {float((row_err / bound).max()):.3f}")
             assert diff_err <= 2 * BF16_TOL
+            assert (row_err <= bound).all()
 
 
 def test_workload_qwen_32k_sampled_rows():

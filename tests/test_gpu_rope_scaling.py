@@ -101,11 +101,7 @@ def test_prefill_bf16_explicit_widths(d, rule):
     table = _explicit_widths(d, 40 + d, 600)
     sc = {"widths": table} if rule is None else dict(SMALL_LLAMA3, widths=table)
     say(f"prefill bf16 explicit widths d={d} rule={rule}")
-    # seed 41 gave 1.03e-2 here for d = 64 with the llama3 rule: one output of
-    # 2.287 on row 1, where bf16 values are 1/64 apart and the fp32 result sat
-    # 2.5e-3 past the rounding midpoint (rotated operands and P are rounded to
-    # bf16 for the MFMAs); the tail of the bf16 error, not a wrong window
-    q, k, v = synth.prefill_inputs(2, 4, 2, 700, 700, d, torch.bfloat16, 51, device="cuda")
+    q, k, v = synth.prefill_inputs(2, 4, 2, 700, 700, d, torch.bfloat16, 41, device="cuda")
     out = atw.prefill(q, k, v, rope_base=1e4, k_turns=0.0, rope_scaling=sc)
     sync()
     ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, 0.0, scaling=sc)

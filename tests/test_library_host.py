@@ -145,9 +145,10 @@ def test_invalid_arguments(lib):
     hmap = binding._arr32([0, 1, 2, 0])  # kv head 2 does not exist
     assert lib.atw_prefill(fake, fake, fake, fake, 1, 1, 10, 10, 0, 4, 2, hmap, 128, s, s, s, s, 1e4,
                            4.0, 1, 1, 0.0, fake, 1 << 40, None) == atw.binding.ATW_EINVAL
-    # workspace: bf16 needs one packed copy of K and V (64-key tiles), fp32 none
+    # workspace: bf16 needs one packed copy of K and V (64-key tiles) and the
+    # range maxima (32 chunks x 2 words per (batch, kv head)), fp32 none
     need = lib.atw_prefill_workspace_bytes(1, 1, 2, 10, 128)
-    assert need == 2 * 1 * 2 * 1 * 64 * 128 * 2
+    assert need == 2 * 1 * 2 * 1 * 64 * 128 * 2 + 1 * 2 * 32 * 2 * 4
     assert lib.atw_prefill_workspace_bytes(0, 1, 2, 10, 128) == 0
     assert pre(ws=need - 1) == atw.binding.ATW_EWORKSPACE
 
@@ -361,3 +362,29 @@ def test_decode_sparse_invalid_arguments(lib):
     assert dec(mask=ctypes.c_void_p(18)) == atw.binding.ATW_EINVAL
     assert dec(words=2) == atw.binding.ATW_EINVAL
     assert b"mask_words" in lib.atw_last_error()
+
+
+def test_rope_flags_contract(lib):
+    """atw_rope.flags: widths is read only under ATW_ROPE_HAS_WIDTHS (a caller
+    of the 0.1 layout, whose word here was a reserved 0, never has a stale
+    pointer read); the flag with a NULL table and unknown bits are rejected."""
+    d = 8
+    out = (ctypes.c_int64 * (d // 2))()
+    plain = atw.window_widths(d, 1e4, 1.0, True)
+    r = binding.Rope()
+    r.kind = binding.ATW_ROPE_PLAIN
+    r.base = 1e4
+    table = (ctypes.c_int64 * (d // 2))(0, 1, 2, 3)
+    r.widths = ctypes.cast(table, ctypes.POINTER(ctypes.c_int64))
+    # flag clear: the pointer is ignored, windows come from k
+    assert lib.atw_window_widths_rope(ctypes.byref(r), d, 1.0, 1, out) == binding.ATW_OK
+    assert list(out) == plain
+    r.flags = binding.ATW_ROPE_HAS_WIDTHS
+    assert lib.atw_window_widths_rope(ctypes.byref(r), d, 1.0, 1, out) == binding.ATW_OK
+    assert list(out) == [0, 1, 2, 3]
+    r.widths = ctypes.cast(None, ctypes.POINTER(ctypes.c_int64))
+    assert lib.atw_window_widths_rope(ctypes.byref(r), d, 1.0, 1, out) == binding.ATW_EINVAL
+    r.widths = ctypes.cast(table, ctypes.POINTER(ctypes.c_int64))
+    for bad in (2, 4, -1):
+        r.flags = bad
+        assert lib.atw_window_widths_rope(ctypes.byref(r), d, 1.0, 1, out) == binding.ATW_EINVAL
