@@ -94,29 +94,35 @@ extern "C" {
  * the windows grow with r and the kept pairs at any distance are a suffix);
  * otherwise the call returns ATW_EINVAL.
  *
- * widths (optional, any kind): when non-NULL, d/2 integer windows W_r (host
- * memory, read during the call only) used in place of floor(k * 2*pi /
- * theta_r); k_turns is then not used.  The rotation still uses theta_r.  Each
- * W_r must be >= 0 and non-decreasing in r (ATW_EINVAL otherwise); values
- * above ATW_UNBOUNDED mean unbounded.  With the window off every pair is kept
- * as usual.  This is for windows tuned or stored per model rather than
- * derived from k.
+ * widths (optional, any kind): read only when flags has ATW_ROPE_HAS_WIDTHS
+ * set; then d/2 integer windows W_r (host memory, read during the call only)
+ * used in place of floor(k * 2*pi / theta_r); k_turns is then not used.  The
+ * rotation still uses theta_r.  Each W_r must be >= 0 and non-decreasing in
+ * r (ATW_EINVAL otherwise); values above ATW_UNBOUNDED mean unbounded.  With
+ * the window off every pair is kept as usual.  This is for windows tuned or
+ * stored per model rather than derived from k.
+ *
+ * flags: ATW_ROPE_HAS_WIDTHS or 0; any other bit set returns ATW_EINVAL.
+ * (Layout note: library version 0.1 had no widths member and required this
+ * word, then named reserved, to be 0; a caller built against that layout
+ * therefore never has widths read past the end of its struct.)
  */
 #define ATW_ROPE_PLAIN 0
 #define ATW_ROPE_LINEAR 1
 #define ATW_ROPE_LLAMA3 2
 #define ATW_ROPE_TABLE 3
+#define ATW_ROPE_HAS_WIDTHS 1   /* atw_rope.flags: the widths member is valid */
 
 typedef struct atw_rope {
   int32_t kind;                 /* ATW_ROPE_* */
-  int32_t reserved;             /* 0 */
+  int32_t flags;                /* ATW_ROPE_HAS_WIDTHS or 0 */
   double base;                  /* PLAIN, LINEAR, LLAMA3: > 1 */
   double factor;                /* LINEAR, LLAMA3: > 0 */
   double low_freq_factor;       /* LLAMA3: > 0 */
   double high_freq_factor;      /* LLAMA3: > low_freq_factor */
   double original_max_position; /* LLAMA3: > 0 */
   const double* theta;          /* TABLE: d/2 frequencies (host) */
-  const int64_t* widths;        /* optional: d/2 explicit windows W_r (host), or NULL */
+  const int64_t* widths;        /* with ATW_ROPE_HAS_WIDTHS: d/2 explicit windows W_r (host) */
 } atw_rope;
 
 /* theta_r of every pair of a descriptor (d/2 values, host) -- host only. */
@@ -206,8 +212,12 @@ int atw_decode_sparse(const void* q, const void* k_cache, const void* v_cache, v
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   workspace: device buffer of at least atw_prefill_workspace_bytes(...)
  *     bytes (ATW_BF16: the keys rotated once and the values, both re-ordered
- *     into matrix-core operand order, 64-key tiles; ATW_F32: none needed, may
+ *     into matrix-core operand order, 64-key tiles, as fp16 scaled by a power
+ *     of two per (batch, kv head) when |k| or |v| reaches 2^14, plus the
+ *     per-chunk maxima that choose those scales; ATW_F32: none needed, may
  *     be NULL).  Contents on entry are ignored; overwritten by the call.
+ *   ATW_BF16 arithmetic: matrix-core operands fp16 (rotated queries and keys,
+ *     values, softmax weights), accumulation fp32, output bf16.
  * Requires n_q >= 0, n_kv >= 1, q_pos0 >= 0, h_q % h_kv == 0 without a map,
  * rope_base > 1, k_turns > 0 when window_on, batch <= 65535.  n_q = 0
  * launches nothing.
@@ -270,7 +280,8 @@ int atw_pruned_terms_sparse(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h
                             const uint32_t* block_mask, int64_t* pruned, int64_t* total);
 
 /* Workspace bytes atw_prefill needs: ATW_BF16: 2 * batch * h_kv *
- * ceil(n_kv / 64) * 64 * head_dim * 2 (one copy of K and V); ATW_F32: 0. */
+ * ceil(n_kv / 64) * 64 * head_dim * 2 (one copy of K and V) + batch * h_kv *
+ * 256 (range maxima); ATW_F32: 0. */
 size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,
                                    int32_t head_dim);
 
@@ -432,8 +443,9 @@ int atw_window_plan_device(int32_t head_dim, double rope_base, double k_turns, i
 /* Message of the last error on the calling thread ("" if none). */
 const char* atw_last_error(void);
 
-/* Library version string ("atw 0.2 (gfx950)": atw_rope carries the optional
- * widths pointer since 0.2). */
+/* Library version string ("atw 0.3 (gfx950)": atw_rope carries the optional
+ * widths pointer since 0.2, read only under ATW_ROPE_HAS_WIDTHS since 0.3;
+ * bf16 prefill and decode use fp16 matrix-core operands since 0.3). */
 const char* atw_version(void);
 
 #ifdef __cplusplus

@@ -29,11 +29,12 @@ EXPORTED = [
 SPARSE_BLOCK = 64
 
 ATW_ROPE_PLAIN, ATW_ROPE_LINEAR, ATW_ROPE_LLAMA3, ATW_ROPE_TABLE = 0, 1, 2, 3
+ATW_ROPE_HAS_WIDTHS = 1
 
 
 class Rope(ctypes.Structure):
     """Mirror of struct atw_rope (include/atw.h)."""
-    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("base", ctypes.c_double),
+    _fields_ = [("kind", ctypes.c_int32), ("flags", ctypes.c_int32), ("base", ctypes.c_double),
                 ("factor", ctypes.c_double), ("low_freq_factor", ctypes.c_double),
                 ("high_freq_factor", ctypes.c_double), ("original_max_position", ctypes.c_double),
                 ("theta", ctypes.POINTER(ctypes.c_double)), ("widths", ctypes.POINTER(ctypes.c_int64))]
@@ -59,6 +60,7 @@ def rope_descriptor(rope_base, rope_scaling, head_dim):
             raise ValueError(f"widths needs head_dim/2 = {head_dim // 2} entries (got {len(wv)})")
         wbuf = (ctypes.c_int64 * len(wv))(*wv)
         r.widths = ctypes.cast(wbuf, ctypes.POINTER(ctypes.c_int64))
+        r.flags = ATW_ROPE_HAS_WIDTHS
         r._keep_widths = wbuf
     kind = rope_scaling.get("rope_type", rope_scaling.get("type"))
     if kind is None or kind == "default":

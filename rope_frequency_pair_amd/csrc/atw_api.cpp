@@ -58,9 +58,14 @@ struct RopeWindow {
 int resolve_rope(const atw_rope* rope, int32_t head_dim, double k_turns, int32_t window_on,
                  int max_dim, RopeWindow* out) {
   if (rope == nullptr) return fail(ATW_EINVAL, "rope is NULL");
+  if (rope->flags & ~ATW_ROPE_HAS_WIDTHS)
+    return fail(ATW_EINVAL, "rope: unknown flags 0x%x", (unsigned)rope->flags);
+  const int64_t* given = (rope->flags & ATW_ROPE_HAS_WIDTHS) ? rope->widths : nullptr;
+  if ((rope->flags & ATW_ROPE_HAS_WIDTHS) && given == nullptr)
+    return fail(ATW_EINVAL, "rope: ATW_ROPE_HAS_WIDTHS with a NULL widths table");
   if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > max_dim)
     return fail(ATW_EINVAL, "head_dim must be even and in 2..%d (got %d)", max_dim, head_dim);
-  if (window_on && rope->widths == nullptr && !(k_turns > 0.0))
+  if (window_on && given == nullptr && !(k_turns > 0.0))
     return fail(ATW_EINVAL, "k_turns must be > 0 when the window is on (got %g)", k_turns);
   atw::RopeSpec spec;
   spec.kind = rope->kind;
@@ -72,8 +77,8 @@ int resolve_rope(const atw_rope* rope, int32_t head_dim, double k_turns, int32_t
   spec.theta = rope->theta;
   const char* why = "";
   if (!atw::rope_theta(spec, head_dim, out->theta, &why)) return fail(ATW_EINVAL, "rope: %s", why);
-  if (rope->widths != nullptr) {
-    if (!atw::explicit_widths(head_dim / 2, rope->widths, window_on != 0, out->widths, &why))
+  if (given != nullptr) {
+    if (!atw::explicit_widths(head_dim / 2, given, window_on != 0, out->widths, &why))
       return fail(ATW_EINVAL, "rope: %s", why);
   } else {
     atw::window_widths_theta(head_dim / 2, out->theta, k_turns, window_on != 0, out->widths);
@@ -160,7 +165,7 @@ extern "C" {
 
 const char* atw_last_error(void) { return g_last_error.c_str(); }
 
-const char* atw_version(void) { return "atw 0.2 (gfx950)"; }
+const char* atw_version(void) { return "atw 0.3 (gfx950)"; }
 
 int atw_window_widths(int32_t head_dim, double rope_base, double k_turns, int32_t window_on,
                       int64_t* widths_out) {
@@ -340,9 +345,10 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   atw::PackParams pk{};
   pk.k = k;
   pk.v = v;
-  const size_t half = need / 2;
+  const size_t tiles = atw::prefill_tile_bytes(batch, h_kv, n_kv, head_dim);
   pk.kp = workspace;
-  pk.vp = static_cast<char*>(workspace) + half;
+  pk.vp = static_cast<char*>(workspace) + tiles;
+  pk.range = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * tiles);
   for (int i = 0; i < 3; ++i) {
     pk.ks[i] = k_strides[i];
     pk.vs[i] = v_strides[i];
@@ -354,6 +360,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   pk.win = p.win;
   p.kp = pk.kp;
   p.vp = pk.vp;
+  p.range = pk.range;
   p.n_kt = pk.n_kt;
   return hip_status(atw::launch_prefill_bf16(p, pk, head_dim, (hipStream_t)stream), "prefill launch");
 }
