@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEADLINE = "llama-3.2-3b-128k"
+CPU_SHARE = 16                # cores of a one-GPU job on the GPU hosts
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_llama128k_traffic.json")
 KERNEL_SOURCES = ["rope_frequency_pair_amd/csrc/prefill.hip", "rope_frequency_pair_amd/csrc/device_common.h"]
 
@@ -124,7 +125,12 @@ def cpu_baseline(sample_rows=256):
 
     from rope_frequency_pair_amd import synth
     w = synth.WORKLOADS[HEADLINE]
-    workers = max(1, min(16, os.cpu_count() or 1, sample_rows))
+    # one single-threaded worker per core this process may run on, capped at
+    # the 16-core share a one-GPU job gets on the GPU hosts (their
+    # os.cpu_count() reports the whole machine)
+    host_cores = os.cpu_count() or 1
+    allowed = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else host_cores
+    workers = max(1, min(CPU_SHARE, allowed, sample_rows))
     rng = np.random.default_rng(0)
     rows = sorted(int(x) for x in rng.integers(w.n // 2, w.n, size=sample_rows))
     # inputs of one (query head, kv head) pair on the CPU generator: same shape,
@@ -150,6 +156,7 @@ def cpu_baseline(sample_rows=256):
     p_all, t_all = oracle.pruned_terms(w.n, w.n, 0, w.head_dim, w.rope_base, w.k_turns)
     full = w.batch * w.h_q * (2 * w.head_dim * (w.n * (w.n + 1) // 2) + 4 * (t_all - p_all))
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": len(args), "kind": "oracle",
+            "host_cores": host_cores, "affinity_cores": allowed, "workers": len(args),
             "sample": f"{len(rows)} query rows (positions {rows[0]}..{rows[-1]}) of one head of the "
                       f"128K Llama-3.2-3B-shaped prefill, window on, float64 numpy; {dt:.1f} s wall; "
                       f"extrapolation to the whole step ({w.h_q} heads x {w.n} rows) at this rate: "
@@ -189,6 +196,42 @@ def decode_profile_run(atw, synth, torch, dev):
                       "banded_line_bytes_on": by_line}), flush=True)
 
 
+def single_profile_run(name, atw, synth, torch, dev):
+    """One workload alone, two window-on launches, for counter runs:
+    qwen32k (head_dim 64 prefill), sparse-independent (128K block-sparse
+    prefill with per-query-block selections), sparse-decode (512K decode over
+    a banded cache with a block selection)."""
+    if name == "qwen32k":
+        wq = synth.WORKLOADS["qwen2.5-0.5b-32k"]
+        q1, k1, v1 = synth.workload_prefill_inputs(wq)
+        o1 = torch.empty_like(q1)
+        for _ in range(2):
+            atw.prefill(q1, k1, v1, rope_base=wq.rope_base, k_turns=wq.k_turns, out=o1)
+    elif name == "sparse-independent":
+        w = synth.WORKLOADS[HEADLINE]
+        q, k, v = synth.workload_prefill_inputs(w)
+        out = torch.empty_like(q)
+        sel = synth.block_selection(w.batch, w.h_q, w.n, w.n, w.seed + 100, vertical=False)
+        smask = atw.pack_block_mask(sel).to(dev)
+        for _ in range(2):
+            atw.prefill_sparse(q, k, v, smask, rope_base=w.rope_base, k_turns=w.k_turns, out=out)
+    elif name == "sparse-decode":
+        wd = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+        qd, kc, vc = synth.workload_decode_inputs(wd)
+        L = wd.n
+        kb = atw.kcache_band(kc)
+        del kc
+        dsel = synth.decode_block_selection(wd.batch, wd.h_kv, L, wd.seed + 100)
+        dmask = atw.pack_block_mask(dsel).to(dev)
+        for _ in range(2):
+            atw.decode_sparse(qd, kb, vc, [L] * wd.batch, [L] * wd.batch, dmask, rope_base=wd.rope_base,
+                              k_turns=wd.k_turns, num_splits=wd.splits, k_banded=True)
+    else:
+        raise SystemExit(f"unknown profile workload {name}")
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": name}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +244,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="profiling: the 512K decode step only (row and banded cache, window on then "
                          "off, two launches each)")
+    ap.add_argument("--profile", choices=["qwen32k", "sparse-independent", "sparse-decode"],
+                    help="profiling: two window-on launches of one more workload only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -228,6 +273,9 @@ def main():
         del src, dst
     if args.decode_only:
         decode_profile_run(atw, synth, torch, dev)
+        return
+    if args.profile:
+        single_profile_run(args.profile, atw, synth, torch, dev)
         return
     log(f"[bench] {atw.version()} on {torch.cuda.get_device_name(0)}; inputs for {w.name}")
     q, k, v = synth.workload_prefill_inputs(w)

@@ -30,7 +30,16 @@
 //    with ordinary loads because each of its lines is covered by two load
 //    instructions that the cache merges;
 //  * the combine pass reads every split's (max, sum) at once, one split per
-//    thread, instead of walking the splits serially.
+//    thread, instead of walking the splits serially;
+//  * QK^T operands are fp16 (v_mfma_f32_16x16x32_f16; 3 more mantissa bits
+//    than bf16): the query scaled by softmax_scale * log2(e) (scores in base
+//    2) with a per-wave power of two if it reaches 2^14, and the rotated keys,
+//    with a per-tile power of two in the rare tile whose largest |k| reaches
+//    2^14 (rotated keys then stay below 2^14.5, inside fp16's 65504); both
+//    powers are undone on the fp32 scores.
+//    P V^T keeps V as stored (bf16) and splits each weight into a bf16 pair
+//    hi + lo (two MFMAs), which carries ~16 bits of the weight: no conversion
+//    of the value stream, no range limit.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -230,16 +239,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const bool col_valid = l16 < G * q_len;
   const int tok = (MULTI && col_valid) ? l16 / G : 0;
   const int col_qh = col_valid ? p.qh_of_kv[g0 + (MULTI ? l16 % G : l16)] : 0;
-  bf16x8 qop[C::NKS];
+  f16x8 qop[C::NKS];
+  int eq;
   {
     const bool valid = col_valid;
     const int qh = col_qh;
     const int tpos = qpos + tok;
     const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + qh * p.qs[1] + tok * p.qs[2];
+    float qt[C::NKS][8];
+    float qmax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const int r0 = 16 * ks + 4 * grp4;
-      u32x4 packed = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qt[ks][e] = 0.f;
       if (valid) {
         const u32x2 a = *reinterpret_cast<const u32x2*>(qrow + r0);
         const u32x2 c2 = *reinterpret_cast<const u32x2*>(qrow + H + r0);
@@ -249,10 +262,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
           const float x2 = (u & 1) ? bf16_hi(c2[u >> 1]) : bf16_lo(c2[u >> 1]);
           float s, c;
           rope_sincos(tpos, p.win.phi[r0 + u], &s, &c);
-          packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
+          qt[ks][2 * u] = (x1 * c - x2 * s) * p.scale_log2;
+          qt[ks][2 * u + 1] = (x2 * c + x1 * s) * p.scale_log2;
+          qmax = fmaxf(qmax, fmaxf(fabsf(qt[ks][2 * u]), fabsf(qt[ks][2 * u + 1])));
         }
       }
-      qop[ks] = __builtin_bit_cast(bf16x8, packed);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+    eq = __builtin_amdgcn_readfirstlane(range_exp_of_float(qmax));
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      u32x4 packed;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        packed[u] = pack_f16(__builtin_amdgcn_ldexpf(qt[ks][2 * u], -eq),
+                             __builtin_amdgcn_ldexpf(qt[ks][2 * u + 1], -eq));
+      qop[ks] = __builtin_bit_cast(f16x8, packed);
     }
   }
 
@@ -325,8 +351,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // last token
   uint32_t rot[MULTI ? C::ROUNDS : 1][8];
   bool nonuni = false;
+  int ek_tile = 0;    // power of two the staged tile's K' carries (wave-uniform)
   auto store_tile = [&](int m0) {
     nonuni = false;
+    // largest |k| of the tile from the loaded bits (bf16 magnitudes compare
+    // as integers): a power of two is needed only if it reaches 2^14
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 kmax = {0, 0};
+#pragma unroll
+    for (int i = 0; i < C::ROUNDS; ++i)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x2, kreg[i][h2][j] & 0x7fff7fffu));
+    uint32_t kmag = max((uint32_t)kmax[0], (uint32_t)kmax[1]);
+    ek_tile = 0;
+    if (__any(kmag >= 0x4680u)) {            // 2^14 as bf16 magnitude bits
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) kmag = max(kmag, (uint32_t)__shfl_xor((int)kmag, o));
+      ek_tile = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(kmag));
+    }
+    const float kscale = __builtin_amdgcn_ldexpf(1.0f, -ek_tile);
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
       const int m = m0 + C::KPR * i + kj;
@@ -345,7 +391,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
         const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
         const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-        uint32_t pk = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
+        float y1 = x1 * rc[e] - x2 * rs[e], y2 = x2 * rc[e] + x1 * rs[e];
+        if (ek_tile != 0) {
+          y1 *= kscale;
+          y2 *= kscale;
+        }
+        uint32_t pk = pack_f16(y1, y2);
         if constexpr (MULTI) {
           rot[i][e] = pk;
           nonuni = nonuni || (dist <= wch[e] && dist + q_len - 1 > wch[e]);
@@ -440,8 +491,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         if (16 * ks + 16 <= r_any) continue;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
-          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[blk], 0, 0, 0);
+          const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[ks], s[blk], 0, 0, 0);
         }
       }
     };
@@ -473,6 +524,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       }
     }
 
+    // the operands' powers of two (queries or keys reaching fp16's range)
+    if (eq + ek_tile != 0) {
+      const float f = __builtin_amdgcn_ldexpf(1.0f, eq + ek_tile);
+      sacc[0] *= f;
+      sacc[1] *= f;
+    }
+
     // keys past the end of the split
     if (m_lo + kTK > k_end) {
 #pragma unroll
@@ -490,28 +548,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sacc[blk][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = half_swap_max(mx);
+    // scores are in base-2 units: the running max and the lazy rescale too
     const float m_new = fmaxf(m_run, mx);
-    const bool grow = (m_new - m_run) * p.scale_log2 > kRescaleLog2;
+    const bool grow = m_new - m_run > kRescaleLog2;
     if (__any(grow)) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * p.scale_log2);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
 #pragma unroll
       for (int i = 0; i < C::ND; ++i) oacc[i] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
-    const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
-    // P^T operand: slots 8*grp4 + e = keys 4grp4 + e (e < 4) and 16 + 4grp4 + e - 4
-    u32x4 pw;
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run;
+    // P^T operand: slots 8*grp4 + e = keys 4grp4 + e (e < 4) and 16 + 4grp4 + e - 4;
+    // each weight as hi + lo, both bf16 (lo = the rounding residue of hi)
+    u32x4 pw, pl;
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i >> 1][2 * (i & 1)], p.scale_log2, -mb));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i >> 1][2 * (i & 1) + 1], p.scale_log2, -mb));
+      const float e0 = __builtin_amdgcn_exp2f(sacc[i >> 1][2 * (i & 1)] - mb);
+      const float e1 = __builtin_amdgcn_exp2f(sacc[i >> 1][2 * (i & 1) + 1] - mb);
       pw[i] = pack_bf16(e0, e1);
-      lsum = sum_bf16x2(pw[i], lsum);      // normalizer of the rounded weights
+      pl[i] = pack_bf16(e0 - bf16_lo(pw[i]), e1 - bf16_hi(pw[i]));
+      lsum = sum_bf16x2(pw[i], lsum);      // normalizer of the weights as multiplied
+      lsum = sum_bf16x2(pl[i], lsum);
     }
     l_run += lsum;
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, pl);
 
     // O^T += V^T P^T: transposing reads give lane l four keys of dim 16bd + l16
 #pragma unroll
@@ -521,12 +584,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       const v4i16 hi = lds_read_tr16(base + 16 * C::VROW);
       const bf16x8 a = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       oacc[bd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, oacc[bd], 0, 0, 0);
+      oacc[bd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, oacc[bd], 0, 0, 0);
     }
     __syncthreads();   // LDS reads done before the next store
     m_cur = m_next;
   }
 
-  // partial result of this split: [m (raw score units), l, -, -, o[D]] per query head
+  // partial result of this split: [m (base-2 score units), l, -, -, o[D]] per query head
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot = half_swap_sum(l_tot);
   if (col_valid) {
@@ -585,7 +649,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   float l = 0.f;
   for (int s = tid; s < S; s += T) {
     const float ms = w[s * (D + 4)];
-    const float a = (ms == -INFINITY) ? 0.f : exp2f((ms - m) * p.scale_log2);
+    const float a = (ms == -INFINITY) ? 0.f : exp2f(ms - m);   // maxima in base-2 units
     weight[s] = a;
     l += a * w[s * (D + 4) + 1];
   }

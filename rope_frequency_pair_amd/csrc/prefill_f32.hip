@@ -1,4 +1,4 @@
-// Windowed causal prefill for gfx950 (MI355X).
+// Windowed causal prefill for fp32 inputs, gfx950 (MI355X).
 //
 // Method: "ATFlash — Per-RoPE-Wavelength Attention Windows", README, "The
 // idea" and "Porting to something else": the window is a slice of the
@@ -16,20 +16,16 @@
 //    blocks of one (batch, kv head), so they share key/value tiles in its L2
 //    (whole kv heads per XCD when they divide evenly, else balanced rounds);
 //  * scores are computed transposed, S^T = K' Q'^T, with
-//    v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2f32), so each
-//    lane holds 16 keys of one query column and the row max / sum are mostly
-//    in-lane; lanes l and l+32 share a query;
-//  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
-//    bf16 k-step of 16 covers 8 whole pairs, so the retained pairs [r, h) are
-//    a contiguous range of k-steps;
-//  * pairs that are in the window for some cells of a wave's tile and not for
-//    others ("partial" pairs) are added first, one pair per MFMA, and after
-//    each such pair the cells beyond its window are reset to zero; because
-//    windows grow with r, this leaves exactly the kept partial terms; the
-//    fully kept pairs are added after;
-//  * O^T += V^T P^T with P^T taken straight from the S^T registers; V is
-//    transposed into LDS (keys contiguous per head-dim row, in the key order
-//    the S^T register layout produces);
+//    v_mfma_f32_32x32x2f32 (one pair-dimension per MFMA), so each lane holds
+//    16 keys of one query column and the row max / sum are mostly in-lane;
+//    lanes l and l+32 share a query (lane half s takes dim r or r + h of
+//    pair r);
+//  * the pairs are taken in ascending order from the tile's first needed
+//    pair; pairs that are in the window for some cells of a wave's tile and
+//    not for others ("partial" pairs) come first, and after each such pair
+//    the cells beyond its window are reset to zero; because windows grow
+//    with r, this leaves exactly the kept partial terms;
+//  * O^T += V^T P^T one key per MFMA, P^T straight from the S^T registers;
 //  * waves 0-3 run each tile as [QK^T, softmax, PV, RoPE staging of the
 //    next tile] and waves 4-7 as [staging, QK^T, softmax, PV], so on each
 //    SIMD the MFMA stretches of one wave meet the VALU stretches of the
@@ -49,48 +45,26 @@ constexpr int kTK = kPrefillTileK;
 constexpr int kReanchor = 16;        // exact RoPE angles every 16 key tiles
 constexpr float kRescaleLog2 = 8.0f;
 
-template <typename T, int D>
+template <int D>
 struct Cfg {
   static constexpr int H = D / 2;
-  static constexpr bool kBf16 = sizeof(T) == 2;
   // K staging: thread = (key tid/8, pair group tid%8) of PPT pairs
   static constexpr int PPT = H / 8;
-  // bf16 K' row: 16-byte quads of 4 pairs; quad qd is stored at unit
-  // (qd % 2) * (H/8) + qd / 2, so the two quads of a k-step live in two
-  // half-row regions and the staging writes of one key are contiguous
-  static constexpr int KROW = D + 16 / (int)sizeof(T);     // elements, 16 B pad
-  // V [64 keys][VROW], row-major as in memory.  bf16 rows are padded so the
-  // row stride is 16 or 48 dwords modulo 64: the transposing reads of four
-  // consecutive rows then hit disjoint banks.  fp32: 4-element pad.
-  static constexpr int VROW = kBf16 ? (D == 128 ? 160 : 96) : (D + 4);
-  static constexpr int NVT = D * (int)sizeof(T) / 128;      // 16-byte V chunks per thread per tile
-  static constexpr int NKS = kBf16 ? D / 16 : H;            // QK^T k-steps
-  static constexpr int ND = D / 32;                         // 32-wide head-dim blocks
+  static constexpr int KROW = D + 4;      // K' row (pairs interleaved), 16-byte pad
+  static constexpr int VROW = D + 4;      // V row, row-major as in memory
+  static constexpr int NVT = D * 4 / 128; // 16-byte V chunks per thread per tile
+  static constexpr int ND = D / 32;       // 32-wide head-dim blocks
 };
 
-template <typename T, int D>
+template <int D>
 struct Smem {
-  T k[2][kTK][Cfg<T, D>::KROW];
-  T v[2][kTK][Cfg<T, D>::VROW];
+  float k[2][kTK][Cfg<D>::KROW];
+  float v[2][kTK][Cfg<D>::VROW];
 };
-
-__device__ __forceinline__ int swap_bits23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
 
 // Key offset (within a 32-key block, before + 4*s) of accumulator register v
 // in the 32x32 MFMA output layout.
 __device__ __forceinline__ constexpr int acc_row(int v) { return 8 * (v >> 2) + (v & 3); }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
-// of the 8 bytes addressed by lanes i/4, i/4+4, i/4+8, i/4+12 (in that order).
-__device__ __forceinline__ v4i16 lds_read_tr16(const void* p) {
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<void*>(p));
-}
 
 // Register chunks of 8, 16 or 32 bytes.
 template <int BYTES>
@@ -125,13 +99,14 @@ __device__ __forceinline__ Chunk<BYTES> zero_chunk() {
   return c;
 }
 
-template <typename T, int D>
+template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParams p) {
-  using C = Cfg<T, D>;
+  using C = Cfg<D>;
+  using T = float;
   constexpr int H = C::H;
   constexpr int PPT = C::PPT;
-  constexpr int KBYTES = PPT * (int)sizeof(T);                 // bytes per half row per K task
-  __shared__ Smem<T, D> sm;
+  constexpr int KBYTES = PPT * 4;                              // bytes per half row per K task
+  __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sh = lane >> 5, l32 = lane & 31;
@@ -190,33 +165,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
 
   // ---- query: load, rotate at its position, keep as MFMA operand
   const T* qrow_ptr = qbase + (int64_t)qrow * p.qs[2];
-  bf16x8 qop[C::kBf16 ? C::NKS : 1];
-  float qf[C::kBf16 ? 1 : H];
-  if constexpr (C::kBf16) {
+  float qf[H];   // lane half s: dim r (s = 0) or r + h (s = 1) of pair r, rotated
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      const int r0 = 8 * ks + 4 * sh;
-      const u32x2 a = *reinterpret_cast<const u32x2*>(qrow_ptr + r0);
-      const u32x2 b = *reinterpret_cast<const u32x2*>(qrow_ptr + H + r0);
-      u32x4 packed;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
-        const float x2 = (u & 1) ? bf16_hi(b[u >> 1]) : bf16_lo(b[u >> 1]);
-        float s, c;
-        rope_sincos(npos, p.win.phi[r0 + u], &s, &c);
-        packed[u] = pack_bf16(x1 * c - x2 * s, x2 * c + x1 * s);
-      }
-      qop[ks] = __builtin_bit_cast(bf16x8, packed);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < H; ++r) {
-      const float x1 = (float)qrow_ptr[r], x2 = (float)qrow_ptr[H + r];
-      float s, c;
-      rope_sincos(npos, p.win.phi[r], &s, &c);
-      qf[r] = sh ? (x2 * c + x1 * s) : (x1 * c - x2 * s);
-    }
+  for (int r = 0; r < H; ++r) {
+    const float x1 = qrow_ptr[r], x2 = qrow_ptr[H + r];
+    float s, c;
+    rope_sincos(npos, p.win.phi[r], &s, &c);
+    qf[r] = sh ? (x2 * c + x1 * s) : (x1 * c - x2 * s);
   }
 
   f32x16 oacc[C::ND];
@@ -234,19 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
   const int kj = lane, kc = ((wave & 3) << 1) | (wave >> 2);
   const T* ksrc = kbase + (int64_t)kj * p.ks[2] + kc * PPT;
   const int64_t kstep = (int64_t)kTK * p.ks[2];
-  int koff0, koff1;                              // LDS element offsets of the K' writes
-  if constexpr (C::kBf16) {
-    if constexpr (PPT == 8) {
-      koff0 = kj * C::KROW + 8 * kc;             // quad 2kc   -> unit kc
-      koff1 = kj * C::KROW + 8 * (H / 8 + kc);   // quad 2kc+1 -> unit H/8 + kc
-    } else {                                     // PPT == 4: quad kc
-      koff0 = kj * C::KROW + 8 * ((kc & 1) * (H / 8) + (kc >> 1));
-      koff1 = koff0;
-    }
-  } else {
-    koff0 = kj * C::KROW + 2 * kc * PPT;         // fp32: pairs interleaved
-    koff1 = koff0;
-  }
+  const int koff0 = kj * C::KROW + 2 * kc * PPT;   // LDS element offset of the K' writes (pairs interleaved)
   // RoPE step over one key tile (64*theta_r) for the wave's pairs: uniform
   float st_c[PPT], st_s[PPT];
 #pragma unroll
@@ -257,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     st_s[e] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s)));
   }
   // V: row-major 16-byte chunks, task = tid + 512*i -> (key, chunk)
-  constexpr int VCH = D * (int)sizeof(T) / 16;   // 16-byte chunks per V row
+  constexpr int VCH = D * 4 / 16;                // 16-byte chunks per V row
   const T* vsrc[C::NVT];
   int voff[C::NVT], vkey[C::NVT];
 #pragma unroll
@@ -265,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     const int task = tid + kThreads * i;
     vkey[i] = task / VCH;
     const int ch = task % VCH;
-    vsrc[i] = vbase + (int64_t)vkey[i] * p.vs[2] + ch * (16 / (int)sizeof(T));
-    voff[i] = vkey[i] * C::VROW + ch * (16 / (int)sizeof(T));
+    vsrc[i] = vbase + (int64_t)vkey[i] * p.vs[2] + ch * 4;
+    voff[i] = vkey[i] * C::VROW + ch * 4;
   }
   const int64_t vstep = (int64_t)kTK * p.vs[2];
 
@@ -280,8 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
     int64_t dmin = 0, dmax = 0;
     if (!tile_distance_range(gn_lo, gn_hi, m_lo, m_hi, causal, &dmin, &dmax)) return H;
-    const int r = wave_pairs_below(w_lane, dmin);
-    return C::kBf16 ? (r & ~7) : r;
+    return wave_pairs_below(w_lane, dmin);
   };
 
   auto load_k = [&](int t) {
@@ -310,29 +252,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     }
     if ((kc + 1) * PPT > stage_lo(t)) {          // uniform over the wave
       T* dst = &sm.k[t & 1][0][0];
-      if constexpr (C::kBf16) {
-        uint32_t w[PPT];
+      float y[2 * PPT];
 #pragma unroll
-        for (int e = 0; e < PPT; ++e) {
-          const uint32_t wa = kreg0.w[e >> 1], wb = kreg1.w[e >> 1];
-          const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-          const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-          w[e] = pack_bf16(x1 * rc[e] - x2 * rs[e], x2 * rc[e] + x1 * rs[e]);
-        }
-        *reinterpret_cast<u32x4*>(dst + koff0) = u32x4{w[0], w[1], w[2], w[3]};
-        if constexpr (PPT == 8) *reinterpret_cast<u32x4*>(dst + koff1) = u32x4{w[4], w[5], w[6], w[7]};
-      } else {
-        float y[2 * PPT];
-#pragma unroll
-        for (int e = 0; e < PPT; ++e) {
-          const float x1 = __uint_as_float(kreg0.w[e]), x2 = __uint_as_float(kreg1.w[e]);
-          y[2 * e] = x1 * rc[e] - x2 * rs[e];
-          y[2 * e + 1] = x2 * rc[e] + x1 * rs[e];
-        }
-#pragma unroll
-        for (int i = 0; i < PPT / 2; ++i)
-          reinterpret_cast<f32x4*>(dst + koff0)[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+      for (int e = 0; e < PPT; ++e) {
+        const float x1 = __uint_as_float(kreg0.w[e]), x2 = __uint_as_float(kreg1.w[e]);
+        y[2 * e] = x1 * rc[e] - x2 * rs[e];
+        y[2 * e + 1] = x2 * rc[e] + x1 * rs[e];
       }
+#pragma unroll
+      for (int i = 0; i < PPT / 2; ++i)
+        reinterpret_cast<f32x4*>(dst + koff0)[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
     }
     // advance the rotation to the next tile's key position
 #pragma unroll
@@ -400,84 +329,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
           }
       };
 
-      if constexpr (C::kBf16) {
-        const T* krow0 = kt + l32 * C::KROW + 8 * sh * (H / 8);
-        const T* krow1 = krow0 + 32 * C::KROW;
-        // pairs kept for every cell: k-steps kk0..NKS-1, taken from the top so
-        // the first MFMA starts from a zero accumulator; the operands of the
-        // next k-step are read from LDS while the current one multiplies
-        const int kk0 = r_full >> 3;
-        if (kk0 < C::NKS) {
-          bf16x8 na0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * (C::NKS - 1));
-          bf16x8 na1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * (C::NKS - 1));
+      const T* krow0 = kt + l32 * C::KROW + sh;
+      const T* krow1 = krow0 + 32 * C::KROW;
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
 #pragma unroll
-          for (int ks = C::NKS - 1; ks >= 0; --ks) {
-            if (ks < kk0) break;
-            const bf16x8 a0 = na0, a1 = na1;
-            if (ks > kk0) {
-              na0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * (ks - 1));
-              na1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * (ks - 1));
-            }
-            u32x4 bw = __builtin_bit_cast(u32x4, qop[ks]);
-            if (ks == kk0 && (r_full & 7)) {   // pairs below r_full of this k-step are partial
-#pragma unroll
-              for (int d = 0; d < 4; ++d)
-                if (8 * ks + 4 * sh + d < r_full) bw[d] = 0u;
-            }
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-            if (ks == C::NKS - 1) {
-              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, f32x16{}, 0, 0, 0);
-              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, f32x16{}, 0, 0, 0);
-            } else {
-              sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, sacc[0], 0, 0, 0);
-              sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, sacc[1], 0, 0, 0);
-            }
-          }
-        } else {
-          sacc[0] = f32x16{};
-          sacc[1] = f32x16{};
-        }
-        // partially windowed pairs [r_any, r_full): one pair per MFMA into a
-        // separate accumulator, ascending, each followed by the reset
-        if (r_any < r_full) {
-          f32x16 x[2] = {f32x16{}, f32x16{}};
-          for (int pp = r_any; pp < r_full; ++pp) {
-            const int ks = pp >> 3, uu = pp & 7;
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow0 + 8 * ks);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow1 + 8 * ks);
-            uint32_t qd = 0u;
-#pragma unroll
-            for (int k2 = 0; k2 < C::NKS; ++k2) {
-              const u32x4 qw = __builtin_bit_cast(u32x4, qop[k2]);
-#pragma unroll
-              for (int d = 0; d < 4; ++d) qd = (k2 == ks && d == (uu & 3)) ? qw[d] : qd;
-            }
-            const bool mine = sh == (uu >> 2);
-            u32x4 bw;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) bw[d] = (mine && d == (uu & 3)) ? qd : 0u;
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-            x[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bop, x[0], 0, 0, 0);
-            x[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bop, x[1], 0, 0, 0);
-            drop_cells(x, pp);
-          }
-          sacc[0] += x[0];
-          sacc[1] += x[1];
-        }
-      } else {
-        const T* krow0 = kt + l32 * C::KROW + sh;
-        const T* krow1 = krow0 + 32 * C::KROW;
-        sacc[0] = f32x16{};
-        sacc[1] = f32x16{};
-#pragma unroll
-        for (int r = 0; r < H; ++r) {
-          if (r < r_any) continue;
-          const float a0 = (float)krow0[2 * r];
-          const float a1 = (float)krow1[2 * r];
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, qf[r], sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, qf[r], sacc[1], 0, 0, 0);
-          if (r < r_full) drop_cells(sacc, r);
-        }
+      for (int r = 0; r < H; ++r) {
+        if (r < r_any) continue;
+        const float a0 = krow0[2 * r];
+        const float a1 = krow1[2 * r];
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, qf[r], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, qf[r], sacc[1], 0, 0, 0);
+        if (r < r_full) drop_cells(sacc, r);
       }
 
       // causal and ragged-tail masks (cells outside the attended set)
@@ -513,51 +376,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
       const float mb = (m_run == -INFINITY) ? 0.f : m_run * p.scale_log2;
       float lsum = 0.f;
       const T* vt = &sm.v[t & 1][0][0];
-      if constexpr (C::kBf16) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // V operands of this key group first, so their LDS latency overlaps
-          // the exponentials below.  Transposing reads: lane l gets four keys
-          // of head-dim row 32b + l%32 (the keys of its S^T registers).
-          bf16x8 va[C::ND];
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][v], p.scale_log2, -mb));
+          lsum += e;
+          const int key = 32 * blk + acc_row(v) + 4 * sh;
 #pragma unroll
           for (int b = 0; b < C::ND; ++b) {
-            const T* base = vt + (16 * g + 4 * sh + ((lane & 15) >> 2)) * C::VROW + 32 * b +
-                            16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const v4i16 lo = lds_read_tr16(base);
-            const v4i16 hi = lds_read_tr16(base + 8 * C::VROW);
-            va[b] = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            const float a = vt[key * C::VROW + 32 * b + l32];
+            oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, e, oacc[b], 0, 0, 0);
           }
-          u32x4 pw;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v0 = 8 * (g & 1) + 2 * i;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0], p.scale_log2, -mb));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g >> 1][v0 + 1], p.scale_log2, -mb));
-            pw[i] = pack_bf16(e0, e1);
-            // the normalizer sums the same rounded weights the PV product uses
-            lsum = sum_bf16x2(pw[i], lsum);
-          }
-          const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-          for (int b = 0; b < C::ND; ++b)
-            oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[b], pop, oacc[b], 0, 0, 0);
         }
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][v], p.scale_log2, -mb));
-            lsum += e;
-            const int key = 32 * blk + acc_row(v) + 4 * sh;
-#pragma unroll
-            for (int b = 0; b < C::ND; ++b) {
-              const float a = (float)vt[key * C::VROW + 32 * b + l32];
-              oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, e, oacc[b], 0, 0, 0);
-            }
-          }
-      }
       l_run += lsum;
     }
 
@@ -581,14 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
         const int d0 = 32 * b + 8 * v4 + 4 * sh;
         const float y0 = oacc[b][4 * v4] * inv, y1 = oacc[b][4 * v4 + 1] * inv;
         const float y2 = oacc[b][4 * v4 + 2] * inv, y3 = oacc[b][4 * v4 + 3] * inv;
-        if constexpr (C::kBf16) {
-          u32x2 w;
-          w[0] = pack_bf16(y0, y1);
-          w[1] = pack_bf16(y2, y3);
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
-        } else {
-          *reinterpret_cast<f32x4*>(orow + d0) = f32x4{y0, y1, y2, y3};
-        }
+        *reinterpret_cast<f32x4*>(orow + d0) = f32x4{y0, y1, y2, y3};
       }
   }
 }
@@ -600,9 +424,9 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int head_dim, hipStream_t 
   if (blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)blocks), block(kThreads);
   if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<float, 128>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<128>), grid, block, 0, stream, p);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_kernel<float, 64>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<64>), grid, block, 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

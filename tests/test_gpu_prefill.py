@@ -171,6 +171,10 @@ def test_empty_and_tiny():
     dict(n_q=256, n_kv=1300, p0=1044, causal=True, tq=32, tk=64, d=64, base=1e6, k=8.0),
     dict(n_q=200, n_kv=333, p0=0, causal=False, tq=32, tk=64, d=64, base=1e4, k=0.5),
     dict(n_q=1000, n_kv=1000, p0=0, causal=True, tq=17, tk=23, d=32, base=100.0, k=0.4),
+    # the workgroup x key-tile geometry the bf16 prefill stages by (head_dim
+    # 128: 12 waves x 32 rows; head_dim 64: 8 waves x 32 rows)
+    dict(n_q=1000, n_kv=1000, p0=0, causal=True, tq=384, tk=64, d=128, base=1e4, k=0.35),
+    dict(n_q=700, n_kv=1500, p0=800, causal=True, tq=256, tk=64, d=64, base=1e4, k=0.5),
 ])
 def test_device_plan_bit_exact(case):
     """Per-tile pair ranges and pruned counts from the kernels' device code equal
