@@ -40,6 +40,8 @@
 //    P V^T keeps V as stored (bf16) and splits each weight into a bf16 pair
 //    hi + lo (two MFMAs), which carries ~16 bits of the weight: no conversion
 //    of the value stream, no range limit.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -373,48 +375,64 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       ek_tile = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(kmag));
     }
     const float kscale = __builtin_amdgcn_ldexpf(1.0f, -ek_tile);
-#pragma unroll
-    for (int i = 0; i < C::ROUNDS; ++i) {
-      const int m = m0 + C::KPR * i + kj;
-      // exact angles every kReanchorRounds rounds, and (sparse) at the start
-      // of every selected block, after which keys are no longer consecutive
-      const bool anchor = SPARSE ? (i == 0 && (m0 & (kSparseBlock - 1)) == 0)
-                                 : (round_ix % kReanchorRounds == 0);
-      if (anchor) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rope_sincos(m, p.win.phi[kc * 8 + e], &rs[e], &rc[e]);
-      }
-      const int dist = key_dist(m);
-      u32x4 o0, o1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
-        const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-        const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-        float y1 = x1 * rc[e] - x2 * rs[e], y2 = x2 * rc[e] + x1 * rs[e];
-        if (ek_tile != 0) {
-          y1 *= kscale;
-          y2 *= kscale;
-        }
-        uint32_t pk = pack_f16(y1, y2);
-        if constexpr (MULTI) {
-          rot[i][e] = pk;
-          nonuni = nonuni || (dist <= wch[e] && dist + q_len - 1 > wch[e]);
-        }
-        pk = dist > wch[e] ? 0u : pk;             // pair beyond its window at this key
-        if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
-      }
-      __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
-      reinterpret_cast<u32x4*>(dst)[0] = o0;
-      reinterpret_cast<u32x4*>(dst)[1] = o1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float c = rc[e], s = rs[e];
-        rc[e] = c * st_c[e] - s * st_s[e];
-        rs[e] = s * st_c[e] + c * st_s[e];
-      }
-      ++round_ix;
+    // Per-key window zeroing is needed only where some pair's window ends
+    // inside the tile (and for draft tokens, whose distances differ).
+    // Elsewhere every key keeps the same pairs: those below the tile's
+    // r_any are masked out of the query operand instead (K' there holds
+    // finite rotated keys or zeros), and the rest are kept.
+    bool per_key = MULTI;
+    if constexpr (!MULTI) {
+      int64_t dmin = 0, dmax = 0;
+      tile_distance_range(qpos, qpos, m0, min(m0 + kTK - 1, k_end - 1), causal, &dmin, &dmax);
+      per_key = wave_pairs_below(w_lane, dmin) != wave_pairs_below(w_lane, dmax);
     }
+    auto rounds = [&](auto window_keys) {
+      constexpr bool WK = decltype(window_keys)::value;
+#pragma unroll
+      for (int i = 0; i < C::ROUNDS; ++i) {
+        const int m = m0 + C::KPR * i + kj;
+        // exact angles every kReanchorRounds rounds, and (sparse) at the start
+        // of every selected block, after which keys are no longer consecutive
+        const bool anchor = SPARSE ? (i == 0 && (m0 & (kSparseBlock - 1)) == 0)
+                                   : (round_ix % kReanchorRounds == 0);
+        if (anchor) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rope_sincos(m, p.win.phi[kc * 8 + e], &rs[e], &rc[e]);
+        }
+        const int dist = key_dist(m);
+        u32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
+          const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
+          const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+          float y1 = x1 * rc[e] - x2 * rs[e], y2 = x2 * rc[e] + x1 * rs[e];
+          if (ek_tile != 0) {
+            y1 *= kscale;
+            y2 *= kscale;
+          }
+          uint32_t pk = pack_f16(y1, y2);
+          if constexpr (MULTI) {
+            rot[i][e] = pk;
+            nonuni = nonuni || (dist <= wch[e] && dist + q_len - 1 > wch[e]);
+          }
+          if constexpr (WK) pk = dist > wch[e] ? 0u : pk;   // pair beyond its window at this key
+          if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
+        }
+        __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
+        reinterpret_cast<u32x4*>(dst)[0] = o0;
+        reinterpret_cast<u32x4*>(dst)[1] = o1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = rc[e], s = rs[e];
+          rc[e] = c * st_c[e] - s * st_s[e];
+          rs[e] = s * st_c[e] + c * st_s[e];
+        }
+        ++round_ix;
+      }
+    };
+    if (per_key) rounds(std::true_type{});
+    else rounds(std::false_type{});
 #pragma unroll
     for (int i = 0; i < C::NVT; ++i) {
       const int task = lane + 64 * i;
@@ -489,10 +507,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
         if (16 * ks + 16 <= r_any) continue;
+        // the k-step holding r_any: its slots of pairs below r_any (pruned
+        // for every key of the tile) are masked in the query operand (draft
+        // tokens: every key is windowed at staging instead)
+        f16x8 qo = qop[ks];
+        if (!MULTI && 16 * ks < r_any) {
+          u32x4 w = __builtin_bit_cast(u32x4, qo);
+          const int tau = r_any - 16 * ks - 4 * grp4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[u] = u < tau ? 0u : w[u];
+          qo = __builtin_bit_cast(f16x8, w);
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
           const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.k[16 * blk + l16][32 * ks + 8 * grp4]);
-          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[ks], s[blk], 0, 0, 0);
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qo, s[blk], 0, 0, 0);
         }
       }
     };
