@@ -320,6 +320,32 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
 size_t atw_decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t head_dim, int32_t num_splits);
 
 /*
+ * atw_decode_noalloc -- atw_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, result and kernels, without the
+ * workspace.  The per-split partials go to a device array the library holds
+ * on each GPU it runs on until the process ends (atw_decode_noalloc_max_bytes()
+ * = 16 MiB); its address is looked up on the first call on each device.  The
+ * call allocates nothing.
+ *   Returns ATW_EWORKSPACE, before any launch, when the partials
+ *   (atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits)) exceed the
+ *   array.  Every call on one GPU uses that GPU's one array: calls that overlap
+ *   in time on one GPU (other streams, other threads) race and must not be
+ *   issued; calls in one stream are ordered and safe.  Each call writes every
+ *   partial it reads, so nothing carries over from an earlier call.
+ */
+int atw_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                       int64_t batch, const int64_t* kv_len, const int64_t* q_pos,
+                       int32_t h_q, int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                       const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                       const int64_t* o_strides,
+                       double rope_base, double k_turns, int32_t causal, int32_t window_on,
+                       double softmax_scale, int32_t num_splits, void* stream);
+
+/* Bytes of atw_decode_noalloc's per-device array (the largest partials it takes). */
+size_t atw_decode_noalloc_max_bytes(void);
+
+/*
  * atw_decode_banded -- atw_decode over a pair-banded K cache.  The memory
  * system of this GPU moves whole 128-byte lines; in the row layout every line
  * of a key row holds dims of all pairs, so skipping the out-of-window pairs

@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     decode_banded,
     decode_multi,
     decode_multi_workspace_bytes,
+    decode_noalloc,
+    decode_noalloc_max_bytes,
     decode_sparse,
     kcache_band,
     pack_block_mask,

@@ -23,7 +23,7 @@ EXPORTED = [
     "atw_version", "atw_rope_theta", "atw_window_widths_rope", "atw_pruned_terms_rope",
     "atw_prefill_rope", "atw_decode_rope", "atw_decode_banded_rope", "atw_decode_multi",
     "atw_decode_multi_workspace_bytes", "atw_prefill_sparse", "atw_block_mask_words",
-    "atw_pruned_terms_sparse", "atw_decode_sparse",
+    "atw_pruned_terms_sparse", "atw_decode_sparse", "atw_decode_noalloc", "atw_decode_noalloc_max_bytes",
 ]
 
 SPARSE_BLOCK = 64
@@ -122,6 +122,10 @@ def load_library(path=LIB_PATH):
     lib.atw_decode.restype = ctypes.c_int
     lib.atw_decode_banded.argtypes = lib.atw_decode.argtypes
     lib.atw_decode_banded.restype = ctypes.c_int
+    lib.atw_decode_noalloc.argtypes = lib.atw_decode.argtypes[:22] + [_vp]
+    lib.atw_decode_noalloc.restype = ctypes.c_int
+    lib.atw_decode_noalloc_max_bytes.argtypes = []
+    lib.atw_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.atw_kcache_band.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _pi64, _pi64, _vp]
     lib.atw_kcache_band.restype = ctypes.c_int
     lib.atw_decode_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
@@ -465,6 +469,32 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
         float(scale or 0.0), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return out
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, causal=True, window_on=True,
+                   scale=None, num_splits=64, kv_head_of_q=None, out=None, stream=None):
+    """decode() through atw_decode_noalloc: no workspace; the split partials
+    live in the library's per-device array (decode_noalloc_max_bytes())."""
+    import torch
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    kv_len = [int(x) for x in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
+    q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
+    _check(lib.atw_decode_noalloc(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
+        _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
+        _arr64(out.stride()[:2]), float(rope_base), float(k_turns), int(causal), int(window_on),
+        float(scale or 0.0), int(num_splits), _stream_ptr(stream)))
+    return out
+
+
+def decode_noalloc_max_bytes():
+    return int(load_library().atw_decode_noalloc_max_bytes())
 
 
 def decode_sparse(q, k_cache, v_cache, kv_len, q_pos, block_mask, *, rope_base, k_turns, causal=True,

@@ -576,6 +576,27 @@ int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                      stream, false);
 }
 
+int atw_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
+                       int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
+                       int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,
+                       const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                       const int64_t* o_strides, double rope_base, double k_turns, int32_t causal,
+                       int32_t window_on, double softmax_scale, int32_t num_splits, void* stream) {
+  const size_t need = atw_decode_workspace_bytes(batch, h_q, head_dim, num_splits);
+  if (need > atw::kDecodeScratchBytes)
+    return fail(ATW_EWORKSPACE,
+                "atw_decode_noalloc: the split partials need %zu bytes, more than its %zu-byte device "
+                "array (use fewer splits or atw_decode with a workspace)",
+                need, (size_t)atw::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if (int e = hip_status(atw::decode_scratch(&scratch), "decode scratch lookup")) return e;
+  return atw_decode(q, k_cache, v_cache, o, dtype, batch, kv_len, q_pos, h_q, h_kv, kv_head_of_q,
+                    head_dim, q_strides, k_strides, v_strides, o_strides, rope_base, k_turns, causal,
+                    window_on, softmax_scale, num_splits, scratch, atw::kDecodeScratchBytes, stream);
+}
+
+size_t atw_decode_noalloc_max_bytes(void) { return atw::kDecodeScratchBytes; }
+
 int atw_decode_rope(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
                     int64_t batch, const int64_t* kv_len, const int64_t* q_pos, int32_t h_q,
                     int32_t h_kv, const int32_t* kv_head_of_q, int32_t head_dim,

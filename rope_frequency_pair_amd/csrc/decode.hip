@@ -40,6 +40,7 @@
 //    P V^T keeps V as stored (bf16) and splits each weight into a bf16 pair
 //    hi + lo (two MFMAs), which carries ~16 bits of the weight: no conversion
 //    of the value stream, no range limit.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -745,6 +746,34 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipSt
 #undef ATW_DECODE_ALL
 #undef ATW_DECODE_SPLIT
   return hipGetLastError();
+}
+
+// Split partials of the allocation-free decode entry point: one file-scope
+// array per GPU (each device holds its own copy of it for the life of the
+// process).  Host code never uses the array's name as an address: the
+// device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept.
+namespace {
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = addr;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_kcache_band(const BandParams& p, int head_dim, hipStream_t stream) {

@@ -120,6 +120,12 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, const PackParams& pk, int
                                hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool banded, hipStream_t stream);
 hipError_t launch_kcache_band(const BandParams& p, int head_dim, hipStream_t stream);
+
+// Size of the device array that holds the split partials of the
+// allocation-free decode entry point, and its device address on the current
+// device (looked up on the first call per device, then kept).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 
 }  // namespace atw
