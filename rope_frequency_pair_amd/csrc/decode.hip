@@ -16,14 +16,16 @@
 //    pairs of that key beyond their window (and skips loading pair chunks
 //    that are entirely beyond it), so the window is exact per key with no
 //    extra MFMA work; whole k-steps pruned for a tile are skipped;
-//  * key tiles of 32 keys; a lane owns one 8-pair chunk of every 8th key
-//    (16th for d = 64), so its RoPE angle advances by a constant per round
-//    (rotation recurrence, re-anchored exactly every 64 rounds);
+//  * key tiles of 32 keys; in a staging round a lane owns one 8-pair chunk
+//    of one key, the same chunk of every 8th key (16th for d = 64) from round
+//    to round, so its RoPE angle advances by a constant per round (rotation
+//    recurrence, re-anchored exactly every 64 rounds); draft tokens stage
+//    only the chunks some key of the tile keeps, in fewer rounds;
 //  * the next tile's K chunks and V rows are loaded into registers while the
 //    current tile is computed from LDS; V stays row-major in LDS and is read
 //    into the PV operand with the transposing LDS read;
-//  * about 180 VGPRs and 20 KB of LDS per wave: 8 waves per CU, each with a
-//    16 KB tile in flight;
+//  * about 240 VGPRs (d = 128) and 20 KB of LDS per wave: 8 waves per CU,
+//    each with a 16 KB tile in flight;
 //  * the cache streams (row-layout K, V) are read with non-temporal loads,
 //    which stream markedly faster from HBM on this GPU (a plain streaming
 //    read reaches ~7 TB/s with them, ~6.2 TB/s without); the banded K is read
@@ -231,6 +233,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 
   const int g0 = p.kv_first[kvh], G = p.kv_first[kvh + 1] - g0;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
+  // theta_r / 2pi of pair r = lane (the frequencies of other lanes' pairs are
+  // taken from here with lane shuffles: a read of the kernel arguments at a
+  // lane-dependent index is a memory round trip the wave would wait on)
+  const double phi_lane = lane < H ? p.win.phi[lane] : 0.0;
+  auto phi_of = [&](int r) -> double {
+    const uint64_t bits = __builtin_bit_cast(uint64_t, phi_lane);
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)bits, r);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(bits >> 32), r);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  };
 
   const __bf16* kbase = (const __bf16*)p.k + b * p.ks[0] + kvh * p.ks[1];
   const __bf16* vbase = (const __bf16*)p.v + b * p.vs[0] + kvh * p.vs[1];
@@ -254,21 +266,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const int r0 = 16 * ks + 4 * grp4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qt[ks][e] = 0.f;
+      // columns past the kv head's query heads hold zeros; the rotation runs
+      // on every lane (phi_of reads other lanes, which must all be active)
+      u32x2 a = {0u, 0u}, c2 = {0u, 0u};
       if (valid) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(qrow + r0);
-        const u32x2 c2 = *reinterpret_cast<const u32x2*>(qrow + H + r0);
+        a = *reinterpret_cast<const u32x2*>(qrow + r0);
+        c2 = *reinterpret_cast<const u32x2*>(qrow + H + r0);
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
-          const float x2 = (u & 1) ? bf16_hi(c2[u >> 1]) : bf16_lo(c2[u >> 1]);
-          float s, c;
-          rope_sincos(tpos, p.win.phi[r0 + u], &s, &c);
-          qt[ks][2 * u] = (x1 * c - x2 * s) * p.scale_log2;
-          qt[ks][2 * u + 1] = (x2 * c + x1 * s) * p.scale_log2;
-          qmax = fmaxf(qmax, fmaxf(fabsf(qt[ks][2 * u]), fabsf(qt[ks][2 * u + 1])));
-        }
+      for (int u = 0; u < 4; ++u) {
+        const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
+        const float x2 = (u & 1) ? bf16_hi(c2[u >> 1]) : bf16_lo(c2[u >> 1]);
+        float s, c;
+        rope_sincos(tpos, phi_of(r0 + u), &s, &c);
+        qt[ks][2 * u] = (x1 * c - x2 * s) * p.scale_log2;
+        qt[ks][2 * u + 1] = (x2 * c + x1 * s) * p.scale_log2;
+        qmax = fmaxf(qmax, fmaxf(fabsf(qt[ks][2 * u]), fabsf(qt[ks][2 * u + 1])));
       }
     }
 #pragma unroll
@@ -290,18 +303,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   for (int i = 0; i < C::ND; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // K staging: lane = (key offset kj, pair chunk kc); its keys are kj, kj+KPR, ...
-  // (banded: consecutive lanes take consecutive keys of one band)
-  const int kj = BANDED ? lane % C::KPR : lane / C::NCH;
-  const int kc = BANDED ? lane / C::KPR : lane % C::NCH;
-  // RoPE step of one round (KPR keys) for the lane's 8 pairs
-  float st_c[8], st_s[8], rc[8], rs[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) rope_sincos(C::KPR, p.win.phi[kc * 8 + e], &st_s[e], &st_c[e]);
-  // windows of the lane's 8 pairs: pair kc*8+e is dropped for a key iff dist > W
-  int wch[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wch[e] = p.win.w[kc * 8 + e];
+  // K staging.  A tile is staged in nr rounds of 32/nr keys, each round
+  // covering the last 2*nr pair chunks of its keys (nr = 1, 2 or ROUNDS); a
+  // lane takes pair chunk kc of key kj (banded: consecutive lanes take
+  // consecutive keys of one band; row cache: consecutive chunks of one key
+  // row).  The chunks before the staged ones must be pruned for every key of
+  // the tile (their longest-window pair already beyond the window at the
+  // tile's nearest key): the QK^T loop skips their k-steps (2 chunks each),
+  // so they need neither loads nor rotations.  nr = 0: every pair is pruned
+  // for the whole tile (scores 0, no K staging).
+  // Draft tokens stage only the chunks the tile needs (far from the query
+  // most tiles then take 1 or 2 rounds): their tiles carry the most VALU
+  // work per byte.  A single token stages every chunk in ROUNDS rounds,
+  // with lanes of pruned chunks idle (no load, a rotation of zeros): its
+  // cache stream comes in faster that way on this GPU (measured), and the
+  // rounds' arithmetic is not what bounds it.
+  auto tile_rounds = [&](int m0) -> int {
+    if constexpr (!MULTI) return C::ROUNDS;
+    int64_t dmin = 0, dmax = 0;
+    tile_distance_range(qpos, qpos, m0, min(m0 + kTK - 1, k_end - 1), causal, &dmin, &dmax);
+    // chunks whose longest-window pair 8c + 7 is pruned at the nearest key
+    const int c0 = __popcll(__ballot((lane & 7) == 7 && (int64_t)w_lane < dmin));
+    const int need = C::NCH - c0;
+    return need <= 0 ? 0 : need <= 2 ? 1 : need <= 4 ? 2 : 4;
+  };
+  auto lane_map = [&](int nr, int* kc, int* kj) {
+    const int sh = nr == 4 ? 2 : nr == 2 ? 1 : 0;   // log2 nr; 32 >> sh keys per round
+    const int c0s = C::NCH - (2 << sh);
+    if constexpr (BANDED) {
+      *kc = c0s + (lane >> (5 - sh));
+      *kj = lane & ((32 >> sh) - 1);
+    } else {
+      *kc = c0s + (lane & ((2 << sh) - 1));
+      *kj = lane >> (1 + sh);
+    }
+  };
 
   u32x4 kreg[C::ROUNDS][2];
   u32x4 vreg[C::NVT];
@@ -312,21 +348,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     return (causal || d >= 0) ? d : -d;
   };
 
+  // lane map of the tile in kreg (set by load_tile)
+  int nr_ld = -1, kc_ld = 0, kj_ld = 0, w7_ld = 0;
   auto load_tile = [&](int m0) {
+    const int nr = tile_rounds(m0);
+    if (nr != nr_ld) {
+      nr_ld = nr;
+      if (nr > 0) {
+        lane_map(nr, &kc_ld, &kj_ld);
+        // from the lanes' windows, not from memory: a load here would leave
+        // every later use waiting on the memory counter behind the tile's loads
+        w7_ld = __shfl(w_lane, kc_ld * 8 + 7);
+      }
+    }
+    const int kpr = kTK / max(nr, 1);
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
-      const int m = m0 + C::KPR * i + kj;
+      if (i >= nr) break;
+      const int m = m0 + kpr * i + kj_ld;
       // the chunk is needed iff its last (longest-window) pair is kept at this key
-      if (m < k_end && key_dist(m) <= wch[7]) {
+      if (m < k_end && key_dist(m) <= w7_ld) {
         if constexpr (BANDED) {
-          const __bf16* src = kbase + (int64_t)kc * p.ks[2] + (int64_t)m * 16;
+          const __bf16* src = kbase + (int64_t)kc_ld * p.ks[2] + (int64_t)m * 16;
           // a lane's two loads are the halves of its key's 32 bytes, so each
           // load instruction covers every other 16 bytes of the band's lines:
           // ordinary loads, so the cache merges the two into one fetch
           kreg[i][0] = *reinterpret_cast<const u32x4*>(src);
           kreg[i][1] = *reinterpret_cast<const u32x4*>(src + 8);
         } else {
-          const __bf16* src = kbase + (int64_t)m * p.ks[2] + kc * 8;
+          const __bf16* src = kbase + (int64_t)m * p.ks[2] + kc_ld * 8;
           // whole lines of the row per instruction: streamed
           kreg[i][0] = load_stream(src);
           kreg[i][1] = load_stream(src + H);
@@ -348,92 +398,121 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   };
 
-  int round_ix = 0;   // staging rounds done so far (drives the recurrence)
-  // MULTI: rotated, packed K' pairs of the staged tile (not yet windowed), and
-  // whether some key of the tile has a pair kept for token 0 but not for the
-  // last token
-  uint32_t rot[MULTI ? C::ROUNDS : 1][8];
-  bool nonuni = false;
-  int ek_tile = 0;    // power of two the staged tile's K' carries (wave-uniform)
+  // Rotation of the staged lane map: the lane's pair chunk kc_st for keys
+  // kj_st + (32/nr) i.  Its angles advance by a constant per round (st_c,
+  // st_s: the angle of 32/nr keys) and are set exactly at the first tile of a
+  // lane map, every kReanchorRounds rounds, and (sparse) at the start of every
+  // selected block, after which keys are no longer consecutive.
+  int nr_st = -1, kc_st = 0, kj_st = 0;
+  float st_c[8], st_s[8], rc[8], rs[8];
+  int wch[8];          // windows of the lane's 8 pairs
+  int since_anchor = 0;
+  int ek_tile = 0;     // power of two the staged tile's K' carries (wave-uniform)
   auto store_tile = [&](int m0) {
-    nonuni = false;
-    // largest |k| of the tile from the loaded bits (bf16 magnitudes compare
-    // as integers): a power of two is needed only if it reaches 2^14
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    u16x2 kmax = {0, 0};
+    const int nr = MULTI ? nr_ld : C::ROUNDS;
+    bool anchor = SPARSE ? (m0 & (kSparseBlock - 1)) == 0 : since_anchor >= kReanchorRounds;
+    if (nr != nr_st) {
+      nr_st = nr;
+      anchor = true;
+      if (nr > 0) {
+        kc_st = kc_ld;
+        kj_st = kj_ld;
 #pragma unroll
-    for (int i = 0; i < C::ROUNDS; ++i)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x2, kreg[i][h2][j] & 0x7fff7fffu));
-    uint32_t kmag = max((uint32_t)kmax[0], (uint32_t)kmax[1]);
+        for (int e = 0; e < 8; ++e) {
+          wch[e] = __shfl(w_lane, kc_st * 8 + e);
+          rope_sincos(kTK / nr, phi_of(kc_st * 8 + e), &st_s[e], &st_c[e]);
+        }
+      }
+    }
     ek_tile = 0;
-    if (__any(kmag >= 0x4680u)) {            // 2^14 as bf16 magnitude bits
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) kmag = max(kmag, (uint32_t)__shfl_xor((int)kmag, o));
-      ek_tile = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(kmag));
-    }
-    const float kscale = __builtin_amdgcn_ldexpf(1.0f, -ek_tile);
-    // Per-key window zeroing is needed only where some pair's window ends
-    // inside the tile (and for draft tokens, whose distances differ).
-    // Elsewhere every key keeps the same pairs: those below the tile's
-    // r_any are masked out of the query operand instead (K' there holds
-    // finite rotated keys or zeros), and the rest are kept.
-    bool per_key = MULTI;
-    if constexpr (!MULTI) {
-      int64_t dmin = 0, dmax = 0;
-      tile_distance_range(qpos, qpos, m0, min(m0 + kTK - 1, k_end - 1), causal, &dmin, &dmax);
-      per_key = wave_pairs_below(w_lane, dmin) != wave_pairs_below(w_lane, dmax);
-    }
-    auto rounds = [&](auto window_keys) {
-      constexpr bool WK = decltype(window_keys)::value;
+    if (nr > 0) {
+      // largest |k| of the staged chunks from the loaded bits (bf16 magnitudes
+      // compare as integers): a power of two is needed only if it reaches 2^14
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      u16x2 kmax = {0, 0};
 #pragma unroll
       for (int i = 0; i < C::ROUNDS; ++i) {
-        const int m = m0 + C::KPR * i + kj;
-        // exact angles every kReanchorRounds rounds, and (sparse) at the start
-        // of every selected block, after which keys are no longer consecutive
-        const bool anchor = SPARSE ? (i == 0 && (m0 & (kSparseBlock - 1)) == 0)
-                                   : (round_ix % kReanchorRounds == 0);
-        if (anchor) {
+        if (i >= nr) break;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rope_sincos(m, p.win.phi[kc * 8 + e], &rs[e], &rc[e]);
-        }
-        const int dist = key_dist(m);
-        u32x4 o0, o1;
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
-          const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-          const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-          float y1 = x1 * rc[e] - x2 * rs[e], y2 = x2 * rc[e] + x1 * rs[e];
-          if (ek_tile != 0) {
-            y1 *= kscale;
-            y2 *= kscale;
-          }
-          uint32_t pk = pack_f16(y1, y2);
-          if constexpr (MULTI) {
-            rot[i][e] = pk;
-            nonuni = nonuni || (dist <= wch[e] && dist + q_len - 1 > wch[e]);
-          }
-          if constexpr (WK) pk = dist > wch[e] ? 0u : pk;   // pair beyond its window at this key
-          if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
-        }
-        __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
-        reinterpret_cast<u32x4*>(dst)[0] = o0;
-        reinterpret_cast<u32x4*>(dst)[1] = o1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float c = rc[e], s = rs[e];
-          rc[e] = c * st_c[e] - s * st_s[e];
-          rs[e] = s * st_c[e] + c * st_s[e];
-        }
-        ++round_ix;
+          for (int j = 0; j < 4; ++j)
+            kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x2, kreg[i][h2][j] & 0x7fff7fffu));
       }
-    };
-    if (per_key) rounds(std::true_type{});
-    else rounds(std::false_type{});
+      uint32_t kmag = max((uint32_t)kmax[0], (uint32_t)kmax[1]);
+      if (__any(kmag >= 0x4680u)) {            // 2^14 as bf16 magnitude bits
+        // rare: scale the loaded keys by 2^-ek in place (exact: a power of two)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) kmag = max(kmag, (uint32_t)__shfl_xor((int)kmag, o));
+        ek_tile = __builtin_amdgcn_readfirstlane(range_exp_of_bf16(kmag));
+        const float f = __builtin_amdgcn_ldexpf(1.0f, -ek_tile);
+#pragma unroll
+        for (int i = 0; i < C::ROUNDS; ++i) {
+          if (i >= nr) break;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t w = kreg[i][h2][j];
+              kreg[i][h2][j] = pack_bf16(bf16_lo(w) * f, bf16_hi(w) * f);
+            }
+        }
+      }
+      // Per-key window zeroing is needed only where some pair's window ends
+      // inside the tile, and for draft tokens (rewritten per token below).
+      // Elsewhere every key keeps the same pairs: those below the tile's
+      // r_any are masked out of the query operand instead (K' there holds
+      // finite rotated keys), and the rest are kept.
+      bool per_key = MULTI;
+      if constexpr (!MULTI) {
+        int64_t dmin = 0, dmax = 0;
+        tile_distance_range(qpos, qpos, m0, min(m0 + kTK - 1, k_end - 1), causal, &dmin, &dmax);
+        per_key = wave_pairs_below(w_lane, dmin) != wave_pairs_below(w_lane, dmax);
+      }
+      const int kpr = kTK / nr;
+      if (anchor) since_anchor = 0;
+      auto rounds = [&](auto window_keys) {
+        constexpr bool WK = decltype(window_keys)::value;
+#pragma unroll
+        for (int i = 0; i < C::ROUNDS; ++i) {
+          if (i >= nr) break;
+          const int m = m0 + kpr * i + kj_st;
+          if (i == 0 && anchor) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rope_sincos(m, phi_of(kc_st * 8 + e), &rs[e], &rc[e]);
+          }
+          const int dist = key_dist(m);
+          u32x4 o0, o1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wa = kreg[i][0][e >> 1], wb = kreg[i][1][e >> 1];
+            const float x1 = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
+            const float x2 = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+            float y1 = x1 * rc[e] - x2 * rs[e], y2 = x2 * rc[e] + x1 * rs[e];
+            // the rotated pair is finished in fp32 and then converted in one
+            // packed conversion: left alone, the compiler fuses each product
+            // and its fp16 rounding into half-register writes (v_fma_mix),
+            // which measured slower here
+            asm volatile("" : "+v"(y1), "+v"(y2));
+            uint32_t pk = pack_f16(y1, y2);
+            if constexpr (WK) pk = dist > wch[e] ? 0u : pk;   // pair beyond its window at this key
+            if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
+          }
+          __bf16* dst = &sm.k[kpr * i + kj_st][16 * kc_st];
+          reinterpret_cast<u32x4*>(dst)[0] = o0;
+          reinterpret_cast<u32x4*>(dst)[1] = o1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float c = rc[e], s = rs[e];
+            rc[e] = c * st_c[e] - s * st_s[e];
+            rs[e] = s * st_c[e] + c * st_s[e];
+          }
+        }
+      };
+      if (per_key) rounds(std::true_type{});
+      else rounds(std::false_type{});
+      since_anchor += nr;
+    }
 #pragma unroll
     for (int i = 0; i < C::NVT; ++i) {
       const int task = lane + 64 * i;
@@ -442,21 +521,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   };
 
-  // MULTI: rewrite the staged K' tile windowed for token j (distance + j)
+  // MULTI: window the staged K' tile (staged for token 0) for token j in
+  // place: a pair dropped at token j - 1 stays dropped at token j (distances
+  // grow with the token index), so token j's tile is token j - 1's with the
+  // pairs whose window ends at the key's token-j distance zeroed as well.
   auto rewrite_k = [&](int m0, int j) {
+    const int nr = MULTI ? nr_st : C::ROUNDS;
+    const int kpr = kTK / max(nr, 1);
 #pragma unroll
     for (int i = 0; i < C::ROUNDS; ++i) {
-      const int m = m0 + C::KPR * i + kj;
+      if (i >= nr) break;
+      const int m = m0 + kpr * i + kj_st;
       const int dist = key_dist(m) + j;
-      u32x4 o0, o1;
+      u32x4* dst = reinterpret_cast<u32x4*>(&sm.k[kpr * i + kj_st][16 * kc_st]);
+      u32x4 o0 = dst[0], o1 = dst[1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t pk = dist > wch[e] ? 0u : rot[MULTI ? i : 0][e];
-        if (e < 4) o0[e] = pk; else o1[e - 4] = pk;
+        if (e < 4) o0[e] = dist > wch[e] ? 0u : o0[e];
+        else o1[e - 4] = dist > wch[e] ? 0u : o1[e - 4];
       }
-      __bf16* dst = &sm.k[C::KPR * i + kj][16 * kc];
-      reinterpret_cast<u32x4*>(dst)[0] = o0;
-      reinterpret_cast<u32x4*>(dst)[1] = o1;
+      dst[0] = o0;
+      dst[1] = o1;
     }
   };
 
@@ -529,9 +614,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     f32x4 sacc[2];
     qk(sacc);
     if constexpr (MULTI) {
-      if (__any(nonuni)) {
-        // some pair's window ends between the tokens' distances in this tile:
-        // recompute for each later token from the rotated values
+      // some pair's window ends between the tokens' distances in this tile
+      // (a window in [dmin, dmax + q_len - 2]): each later token gets its own
+      // pass over the tile, windowed for it
+      if (wave_pairs_below(w_lane, dmin) != wave_pairs_below(w_lane, dmax + q_len - 1)) {
         for (int j = 1; j < q_len; ++j) {
           __syncthreads();
           rewrite_k(m_cur, j);

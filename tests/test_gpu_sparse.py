@@ -177,3 +177,30 @@ def test_sparse_decode_workload_512k_sampled():
         ref = oracle.decode(qn, kn, vn, [L], [L], w.rope_base, w.k_turns, kv_head_of_q=[0] * G,
                             key_blocks=sel[b:b + 1, kvh:kvh + 1].numpy())
         check_rows(to_np(out[b:b + 1, heads]), ref, f"b={b} kv={kvh}")
+
+
+@pytest.mark.parametrize("banded", [False, True])
+def test_sparse_decode_far_apart_blocks(banded):
+    """A selection of a few blocks thousands of blocks apart (one split walks
+    past 64 mask words between two of them, so it reloads the words it holds),
+    against the oracle; sequences with different selections and lengths."""
+    L = 300_000                                  # 4688 blocks, 147 mask words
+    q, kc, vc = synth.decode_inputs(2, 8, 2, L, 128, torch.bfloat16, 74, device="cuda")
+    n_kb = -(-L // 64)
+    sel = torch.zeros((2, 2, n_kb), dtype=torch.bool)
+    sel[0, 0, [0, 2000, n_kb - 1]] = True        # words 0, 62, 146
+    sel[0, 1, [5, 4600]] = True                  # words 0, 143
+    sel[1, 0, [3000]] = True
+    sel[1, 1, [1, 4100, 4101]] = True
+    kv_len = [L, L - 7000]
+    sel[1, :, -(-kv_len[1] // 64):] = False
+    mask = atw.pack_block_mask(sel).cuda()
+    kin = atw.kcache_band(kc) if banded else kc
+    say(f"sparse decode far-apart blocks banded={banded}: oracle")
+    ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, [n - 1 for n in kv_len], 1e6, 4.0,
+                        key_blocks=sel.numpy())
+    for splits in (1, 2, 3):
+        out = atw.decode_sparse(q, kin, vc, kv_len, [n - 1 for n in kv_len], mask, rope_base=1e6,
+                                k_turns=4.0, num_splits=splits, k_banded=banded)
+        sync()
+        check_rows(to_np(out), ref, f"splits={splits} banded={banded}")
