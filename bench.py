@@ -197,7 +197,7 @@ def decode_profile_run(atw, synth, torch, dev):
 
 
 def single_profile_run(name, atw, synth, torch, dev):
-    """One workload alone, two window-on launches, for counter runs:
+    """One workload alone, window-on launches only, for counter runs:
     qwen32k (head_dim 64 prefill), sparse-independent (128K block-sparse
     prefill with per-query-block selections), sparse-decode (512K decode over
     a banded cache with a block selection)."""
@@ -223,9 +223,13 @@ def single_profile_run(name, atw, synth, torch, dev):
         del kc
         dsel = synth.decode_block_selection(wd.batch, wd.h_kv, L, wd.seed + 100)
         dmask = atw.pack_block_mask(dsel).to(dev)
-        for _ in range(2):
+        ws = torch.empty(atw.decode_workspace_bytes(wd.batch, wd.h_q, wd.head_dim, wd.splits),
+                         dtype=torch.uint8, device=dev)
+        od = torch.empty_like(qd)
+        # 2 warm-up + 10 launches: a launch is ~0.1 ms, so a trace needs several
+        for _ in range(12):
             atw.decode_sparse(qd, kb, vc, [L] * wd.batch, [L] * wd.batch, dmask, rope_base=wd.rope_base,
-                              k_turns=wd.k_turns, num_splits=wd.splits, k_banded=True)
+                              k_turns=wd.k_turns, num_splits=wd.splits, k_banded=True, workspace=ws, out=od)
     else:
         raise SystemExit(f"unknown profile workload {name}")
     torch.cuda.synchronize()

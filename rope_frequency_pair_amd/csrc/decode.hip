@@ -138,12 +138,33 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 
 __device__ void sparse_split(const uint32_t* row, int n_words, int nb, int splits, int split,
                              int* first_word, int* first_bit, int* count) {
+  // words are taken kPer per lane (lane l: words 4l .. 4l+3 of a 256-word
+  // chunk), all loads of a chunk issued together: one memory round trip per
+  // chunk and pass, and the first chunk (every row up to 512K keys) is read
+  // once for both passes
+  constexpr int kPer = 4;
+  constexpr int kChunk = 64 * kPer;
   const int lane = threadIdx.x & 63;
-  int total = 0;
-  for (int base = 0; base < n_words; base += 64) {
-    const int wi = base + lane;
-    const uint32_t w = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
-    total += wave_sum_i32(__popc(w));
+  auto load_chunk = [&](int base, uint32_t (&w)[kPer]) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int wi = base + kPer * lane + j;
+      w[j] = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
+    }
+  };
+  auto lane_count = [&](const uint32_t (&w)[kPer]) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c += __popc(w[j]);
+    return c;
+  };
+  uint32_t w0[kPer];
+  load_chunk(0, w0);
+  int total = wave_sum_i32(lane_count(w0));
+  for (int base = kChunk; base < n_words; base += kChunk) {
+    uint32_t w[kPer];
+    load_chunk(base, w);
+    total += wave_sum_i32(lane_count(w));
   }
   const int lo = (int)((int64_t)total * split / splits);
   const int hi = (int)((int64_t)total * (split + 1) / splits);
@@ -152,10 +173,15 @@ __device__ void sparse_split(const uint32_t* row, int n_words, int nb, int split
   *first_bit = 0;
   if (hi <= lo) return;
   int before = 0;
-  for (int base = 0; base < n_words; base += 64) {
-    const int wi = base + lane;
-    const uint32_t w = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
-    const int c = __popc(w);
+  for (int base = 0; base < n_words; base += kChunk) {
+    uint32_t w[kPer];
+    if (base == 0) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) w[j] = w0[j];
+    } else {
+      load_chunk(base, w);
+    }
+    const int c = lane_count(w);
     int incl = c;                                   // inclusive prefix over lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -167,11 +193,20 @@ __device__ void sparse_split(const uint32_t* row, int n_words, int nb, int split
     const uint64_t hit = __ballot(here);
     if (hit) {
       const int src = __builtin_ctzll(hit);
-      // the (lo - before - excl)-th set bit of this lane's word
-      uint32_t rest = w;
-      for (int k = lo - before - excl; k > 0 && rest; --k) rest &= rest - 1u;
-      const int bit = rest ? __builtin_ctz(rest) : 0;
-      *first_word = __shfl(wi, src);
+      // lane src holds the block: the k-th set bit of its kPer words
+      int k = lo - before - excl, word = 0, bit = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int pc = __popc(w[j]);
+        if (k >= 0 && k < pc) {
+          uint32_t rest = w[j];
+          for (int t = k; t > 0; --t) rest &= rest - 1u;
+          word = base + kPer * lane + j;
+          bit = __builtin_ctz(rest);
+        }
+        k -= pc;
+      }
+      *first_word = __shfl(word, src);
       *first_bit = __shfl(bit, src);
       return;
     }
@@ -215,6 +250,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const uint32_t* sel_row = nullptr;
   int sel_word = 0, sel_left = 0;
   uint32_t sel_bits = 0;
+  // the mask words from sel_base on, one per lane, so that moving to the next
+  // selected block is a register lookup instead of a memory round trip
+  int sel_base = 0;
+  uint32_t sel_lane_word = 0;
   const int n_blocks = (kv_len + kSparseBlock - 1) / kSparseBlock;
   if constexpr (SPARSE) {
     sel_row = p.sel + ((int64_t)b * p.h_kv + kvh) * p.sel_words;
@@ -224,9 +263,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     sel_word = __builtin_amdgcn_readfirstlane(sel_word);
     first_bit = __builtin_amdgcn_readfirstlane(first_bit);
     sel_left = __builtin_amdgcn_readfirstlane(sel_left);
-    if (sel_left > 0)
-      sel_bits = __builtin_amdgcn_readfirstlane(sel_row[sel_word]) & valid_bits(sel_word, n_blocks) &
-                 (0xffffffffu << first_bit);
+    sel_base = sel_word;
+    if (sel_left > 0) {
+      const int wi = sel_base + lane;
+      sel_lane_word = wi < p.sel_words ? sel_row[wi] & valid_bits(wi, n_blocks) : 0u;
+      sel_bits = (uint32_t)__builtin_amdgcn_readfirstlane((int)sel_lane_word) & (0xffffffffu << first_bit);
+    }
   } else {
     split_range<D, BANDED>(kv_len, qpos, causal, p.splits, split, p.win.w, &k_begin, &k_end);
   }
@@ -560,8 +602,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       }
       if (sel_left == 0) return -1;
       while (sel_bits == 0) {
-        ++sel_word;
-        sel_bits = __builtin_amdgcn_readfirstlane(sel_row[sel_word]) & valid_bits(sel_word, n_blocks);
+        // the next word with a selected block among the lanes' words after
+        // sel_word; past the last lane, the next 64 words
+        const uint64_t more = __ballot(sel_lane_word != 0u && sel_base + lane > sel_word);
+        if (more != 0) {
+          sel_word = sel_base + (int)__builtin_ctzll(more);
+          sel_bits = (uint32_t)__builtin_amdgcn_readlane((int)sel_lane_word, sel_word - sel_base);
+        } else {
+          sel_base += 64;
+          if (sel_base >= p.sel_words) {    // no word left (sel_left counted only real bits)
+            sel_left = 0;
+            return -1;
+          }
+          sel_word = sel_base - 1;
+          const int wi = sel_base + lane;
+          sel_lane_word = wi < p.sel_words ? sel_row[wi] & valid_bits(wi, n_blocks) : 0u;
+        }
       }
       cur_block = 32 * sel_word + __builtin_ctz(sel_bits);
       sel_bits &= sel_bits - 1u;

@@ -204,3 +204,24 @@ def test_sparse_decode_far_apart_blocks(banded):
                                 k_turns=4.0, num_splits=splits, k_banded=banded)
         sync()
         check_rows(to_np(out), ref, f"splits={splits} banded={banded}")
+
+
+@pytest.mark.parametrize("banded", [False, True])
+def test_sparse_decode_mask_row_past_one_chunk(banded):
+    """A mask row longer than the 256 words the split search reads in one
+    round trip (over 512K keys): selected blocks on both sides of word 256,
+    split starts that fall in the second chunk, against the oracle."""
+    L = 700_000                                  # 10938 blocks, 342 mask words
+    q, kc, vc = synth.decode_inputs(1, 4, 1, L, 128, torch.bfloat16, 75, device="cuda")
+    n_kb = -(-L // 64)
+    sel = torch.zeros((1, 1, n_kb), dtype=torch.bool)
+    sel[0, 0, [3, 8191, 8192, 8193, 9000, 10500, n_kb - 1]] = True   # words 0, 255, 256, 256, 281, 328, 341
+    mask = atw.pack_block_mask(sel).cuda()
+    kin = atw.kcache_band(kc) if banded else kc
+    say(f"sparse decode mask row past one chunk banded={banded}: oracle")
+    ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), [L], [L - 1], 1e6, 4.0, key_blocks=sel.numpy())
+    for splits in (1, 2, 3, 5, 7):
+        out = atw.decode_sparse(q, kin, vc, [L], [L - 1], mask, rope_base=1e6, k_turns=4.0,
+                                num_splits=splits, k_banded=banded)
+        sync()
+        check_rows(to_np(out), ref, f"splits={splits} banded={banded}")
