@@ -97,3 +97,33 @@ def test_decode_multi_workload_512k_sampled(T):
     ref = oracle.decode_multi(to_np(q[:, :, heads]), to_np(kc[:, kvs]), to_np(vc[:, kvs]), kv_len, q_pos,
                               w.rope_base, w.k_turns, kv_head_of_q=hmap)
     check_rows(to_np(out[:, :, heads]), ref, f"T={T}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("banded", [False, True])
+def test_decode_multi_every_staging_regime(d, banded):
+    """Windows short enough (k = 0.01, 0.05) that, walking from the far keys
+    to the near ones, a split passes through tiles where every pair is pruned
+    (scores 0), then through tiles that keep only the last 2, 4 and finally
+    all pair chunks; one split walks all of them, more splits start inside the
+    regimes.  Single-token decode over the same keys (every chunk staged)
+    against the oracle too."""
+    say(f"decode staging regimes d={d} banded={banded}")
+    B, T, Hq, Hkv, L = 2, 3, 6, 2, 3000
+    q, kc, vc = _inputs(B, T, Hq, Hkv, L, d, 77)
+    kv_len = [3000, 1900]
+    q_pos = [3000 - T, 1900 - T]
+    kk = atw.kcache_band(kc) if banded else kc
+    for k_turns in (0.01, 0.05):
+        ref = oracle.decode_multi(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, k_turns)
+        ref1 = oracle.decode(to_np(q[:, 0]), to_np(kc), to_np(vc), [p + 1 for p in q_pos], q_pos, 1e4, k_turns)
+        for splits in (1, 3, 7):
+            out = atw.decode_multi(q, kk, vc, kv_len, q_pos, rope_base=1e4, k_turns=k_turns,
+                                   num_splits=splits, k_banded=banded)
+            sync()
+            check_rows(to_np(out).reshape(-1, d), ref.reshape(-1, d), f"multi k={k_turns} splits={splits}")
+            fn = atw.decode_banded if banded else atw.decode
+            out1 = fn(q[:, 0].contiguous(), kk, vc, [p + 1 for p in q_pos], q_pos, rope_base=1e4,
+                      k_turns=k_turns, num_splits=splits)
+            sync()
+            check_rows(to_np(out1).reshape(-1, d), ref1.reshape(-1, d), f"single k={k_turns} splits={splits}")
