@@ -132,3 +132,36 @@ def test_tile_plan_matches_extremes(n_q, n_kv, q_pos0, causal, tq, tk):
     ref = _plan_from_extremes(n_q, n_kv, q_pos0, causal, tq, tk, w)
     np.testing.assert_array_equal(brute, ref)
     assert np.all(brute[..., 0] <= brute[..., 1])
+
+
+@pytest.mark.parametrize("d,base", [(64, 1e4), (128, 5e5), (128, 1e7)])
+def test_pair_wavelengths_definition(d, base):
+    # lambda_r is the number of positions in one full turn of pair r
+    # ("ATFlash — Per-RoPE-Wavelength Attention Windows", README, "The idea"):
+    # pair 0 turns by 1 radian per position, so lambda_0 = 2*pi exactly; a
+    # shift by lambda_r turns pair r by exactly 2*pi; consecutive pairs'
+    # wavelengths grow by the factor base^(2/d) (60-digit mpmath values)
+    lam = window.pair_wavelengths(d, base)
+    theta = window.pair_frequencies(d, base)
+    assert lam.shape == (d // 2,)
+    assert lam[0] == 2 * math.pi
+    np.testing.assert_allclose(lam * theta, 2 * math.pi, rtol=1e-15)
+    mpmath.mp.dps = 60
+    for r in range(d // 2):
+        ref = 2 * mpmath.pi * mpmath.power(mpmath.mpf(base), mpmath.mpf(2 * r) / d)
+        assert abs(lam[r] - float(ref)) <= 4e-16 * float(ref)
+    np.testing.assert_allclose(lam[1:] / lam[:-1], base ** (2.0 / d), rtol=1e-13)
+
+
+def test_visible_cells_by_hand():
+    # queries at positions 1 and 2 (q_pos0 = 1), keys 0..2
+    vis, dist = window.visible_cells(2, 3, 1, True)
+    assert vis.tolist() == [[True, True, False], [True, True, True]]
+    assert dist[vis].tolist() == [1, 0, 2, 1, 0]
+    # non-causal: every cell visible, distance |n - m|
+    vis, dist = window.visible_cells(2, 3, 1, False)
+    assert vis.all()
+    assert dist.tolist() == [[1, 0, 1], [2, 1, 0]]
+    # queries past the keys (q_pos0 > n_kv): all keys visible
+    vis, dist = window.visible_cells(1, 4, 10, True)
+    assert vis.all() and dist.tolist() == [[10, 9, 8, 7]]
