@@ -9,13 +9,15 @@
 //
 // Work layout (CDNA4 design):
 //  * one workgroup = one wave = one (sequence, kv head, split); the columns
-//    of S^T = K' Q'^T (v_mfma_f32_16x16x32_bf16) are the query heads that read
+//    of S^T = K' Q'^T (v_mfma_f32_16x16x32_f16) are the query heads that read
 //    this kv head (up to 16), so every key is loaded once for all of them;
 //  * all query heads of a decode step sit at one position, so the window of
-//    a cell depends on the key alone: the staging lane of a key zeroes the
-//    pairs of that key beyond their window (and skips loading pair chunks
-//    that are entirely beyond it), so the window is exact per key with no
-//    extra MFMA work; whole k-steps pruned for a tile are skipped;
+//    a cell depends on the key alone: pair chunks entirely beyond a key's
+//    window are not loaded; in a tile where some pair's window ends, the
+//    staging lane of a key zeroes that key's pairs beyond their window, and
+//    elsewhere the pairs pruned for the whole tile are masked in the query
+//    operand, so the window is exact per key with no extra MFMA work; whole
+//    k-steps pruned for a tile are skipped;
 //  * key tiles of 32 keys; in a staging round a lane owns one 8-pair chunk
 //    of one key, the same chunk of every 8th key (16th for d = 64) from round
 //    to round, so its RoPE angle advances by a constant per round (rotation
