@@ -354,8 +354,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   // row).  The chunks before the staged ones must be pruned for every key of
   // the tile (their longest-window pair already beyond the window at the
   // tile's nearest key): the QK^T loop skips their k-steps (2 chunks each),
-  // so they need neither loads nor rotations.  nr = 0: every pair is pruned
-  // for the whole tile (scores 0, no K staging).
+  // so they need neither loads nor rotations.  nr = 0 (draft tokens): every
+  // pair is pruned for the whole tile (scores 0, no K staging).
   // Draft tokens stage only the chunks the tile needs (far from the query
   // most tiles then take 1 or 2 rounds): their tiles carry the most VALU
   // work per byte.  A single token stages every chunk in ROUNDS rounds,
