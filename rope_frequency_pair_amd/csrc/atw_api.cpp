@@ -549,6 +549,12 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   }
   p.kv_first[h_kv] = (int16_t)n;
   p.group = h_q / h_kv;
+  // kv head kv serves query heads kv * group .. kv * group + group - 1, in
+  // order: the kernels then compute a column's query head instead of reading
+  // it from the tables
+  p.heads_in_order = 1;
+  for (int i = 0; i < h_q; ++i)
+    if (p.qh_of_kv[i] != i || kvh[i] != i / p.group) p.heads_in_order = 0;
   if (sparse) {
     p.sel = block_mask;
     p.sel_words = (int32_t)mask_words;

@@ -147,11 +147,17 @@ __device__ void sparse_split(const uint32_t* row, int n_words, int nb, int split
   constexpr int kPer = 4;
   constexpr int kChunk = 64 * kPer;
   const int lane = threadIdx.x & 63;
+  // every lane loads all kPer words (indices past the row clamped to its last
+  // word, n_words >= 1, and their bits dropped afterwards), so the loads carry
+  // no branch and are issued together
   auto load_chunk = [&](int base, uint32_t (&w)[kPer]) {
+    uint32_t x[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x[j] = row[max(0, min(base + kPer * lane + j, n_words - 1))];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int wi = base + kPer * lane + j;
-      w[j] = wi < n_words ? row[wi] & valid_bits(wi, nb) : 0u;
+      w[j] = wi < n_words ? x[j] & valid_bits(wi, nb) : 0u;
     }
   };
   auto lane_count = [&](const uint32_t (&w)[kPer]) {
@@ -247,6 +253,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const int kv_len = p.kv_len[b];
   const int qpos = p.q_pos[b];
   const bool causal = p.causal != 0;
+  // query operand (B of 16x16x32): column l16 = the l16-th query head of this
+  // kv head (MULTI: token l16 / G, head l16 % G), contraction slots 8*grp4.. of
+  // k-step ks = pairs 16ks + 4grp4 + 0..3.  Its loads are issued first, so
+  // their round trip overlaps the split search; columns past the kv head's
+  // query heads hold zeros (the rotation below runs on every lane: phi_of
+  // reads other lanes, which must all be active).
+  // (query heads in model order, the usual grouping: computed, not read from
+  // the head tables, which would put two dependent memory round trips before
+  // the query loads)
+  const bool in_order = p.heads_in_order != 0;
+  const int g0 = in_order ? kvh * p.group : p.kv_first[kvh];
+  const int G = in_order ? p.group : p.kv_first[kvh + 1] - g0;
+  const int q_len = MULTI ? p.q_len : 1;
+  const bool col_valid = l16 < G * q_len;
+  const int tok = (MULTI && col_valid) ? l16 / G : 0;
+  const int col_j = MULTI ? l16 % max(G, 1) : l16;
+  const int col_qh = !col_valid ? 0 : (in_order ? g0 + col_j : p.qh_of_kv[g0 + col_j]);
+  u32x2 qa[C::NKS], qc[C::NKS];
+  {
+    const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + col_qh * p.qs[1] + tok * p.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const int r0 = 16 * ks + 4 * grp4;
+      qa[ks] = u32x2{0u, 0u};
+      qc[ks] = u32x2{0u, 0u};
+      if (col_valid) {
+        qa[ks] = *reinterpret_cast<const u32x2*>(qrow + r0);
+        qc[ks] = *reinterpret_cast<const u32x2*>(qrow + H + r0);
+      }
+    }
+  }
   int k_begin = 0, k_end = kv_len;
   // SPARSE: this split's selected key blocks, walked 32 at a time
   const uint32_t* sel_row = nullptr;
@@ -275,7 +312,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     split_range<D, BANDED>(kv_len, qpos, causal, p.splits, split, p.win.w, &k_begin, &k_end);
   }
 
-  const int g0 = p.kv_first[kvh], G = p.kv_first[kvh + 1] - g0;
   const int w_lane = lane < H ? p.win.w[lane] : kWindowInf;
   // theta_r / 2pi of pair r = lane (the frequencies of other lanes' pairs are
   // taken from here with lane shuffles: a read of the kernel arguments at a
@@ -291,32 +327,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const __bf16* kbase = (const __bf16*)p.k + b * p.ks[0] + kvh * p.ks[1];
   const __bf16* vbase = (const __bf16*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
-  // query operand (B of 16x16x32): column l16 = the l16-th query head of this
-  // kv head (MULTI: token l16 / G, head l16 % G), contraction slots 8*grp4.. of
-  // k-step ks = pairs 16ks + 4grp4 + 0..3
-  const int q_len = MULTI ? p.q_len : 1;
-  const bool col_valid = l16 < G * q_len;
-  const int tok = (MULTI && col_valid) ? l16 / G : 0;
-  const int col_qh = col_valid ? p.qh_of_kv[g0 + (MULTI ? l16 % G : l16)] : 0;
   f16x8 qop[C::NKS];
   int eq;
   {
-    const bool valid = col_valid;
-    const int qh = col_qh;
     const int tpos = qpos + tok;
-    const __bf16* qrow = (const __bf16*)p.q + b * p.qs[0] + qh * p.qs[1] + tok * p.qs[2];
     float qt[C::NKS][8];
     float qmax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const int r0 = 16 * ks + 4 * grp4;
-      // columns past the kv head's query heads hold zeros; the rotation runs
-      // on every lane (phi_of reads other lanes, which must all be active)
-      u32x2 a = {0u, 0u}, c2 = {0u, 0u};
-      if (valid) {
-        a = *reinterpret_cast<const u32x2*>(qrow + r0);
-        c2 = *reinterpret_cast<const u32x2*>(qrow + H + r0);
-      }
+      const u32x2 a = qa[ks], c2 = qc[ks];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float x1 = (u & 1) ? bf16_hi(a[u >> 1]) : bf16_lo(a[u >> 1]);
@@ -781,19 +801,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 }
 
 // Merge the splits of one (sequence, query head): standard online-softmax
-// merge of (max, sum, unnormalised output) partials.  The splits' maxima and
-// weights are read by all threads at once (one split per thread, strided),
-// so the merge costs a few dependent memory round trips, not one per split.
-// The weighted sum of the outputs is spread over G = kCombineThreads / D
-// groups of D threads (group g takes splits g, g + G, ...), whose partial
-// sums meet in LDS: with hundreds of splits and a handful of blocks per
-// call (one sequence, few heads) a single group would walk the splits one
-// memory round trip after another.
+// merge of (max, sum, unnormalised output) partials.  Every partial the
+// merge needs is requested at once, before any of it is used: each thread's
+// split maxima and sums (one split per thread, strided) and the first kPre
+// outputs of its split group, so the merge waits for one memory round trip,
+// not one per dependent step; only splits beyond the first G * kPre are read
+// afterwards.  The weighted sum of the outputs is spread over
+// G = kCombineThreads / D groups of D threads (group g takes splits g, g + G,
+// ...), whose partial sums meet in LDS: with hundreds of splits and a handful
+// of blocks per call (one sequence, few heads) a single group would walk the
+// splits one memory round trip after another.
 constexpr int kCombineThreads = 512;
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams p) {
   constexpr int T = kCombineThreads, NW = T / 64, G = T / D;
+  constexpr int kPre = 16;                                   // outputs requested up front
+  constexpr int kSplitsPerThread = (kMaxDecodeSplits + T - 1) / T;
   __shared__ float weight[kMaxDecodeSplits];
   __shared__ float part[NW];
   __shared__ float gsum[G - 1][D];
@@ -817,20 +841,41 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
     __syncthreads();
     return x;
   };
+  float ms[kSplitsPerThread], ls[kSplitsPerThread], opre[kPre];
+#pragma unroll
+  for (int j = 0; j < kSplitsPerThread; ++j) {
+    const int s = tid + T * j;
+    ms[j] = s < S ? w[s * (D + 4)] : -INFINITY;
+    ls[j] = s < S ? w[s * (D + 4) + 1] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int s = g + G * j;
+    opre[j] = s < S ? w[s * (D + 4) + 4 + d] : 0.f;
+  }
   float m = -INFINITY;
-  for (int s = tid; s < S; s += T) m = fmaxf(m, w[s * (D + 4)]);
+#pragma unroll
+  for (int j = 0; j < kSplitsPerThread; ++j) m = fmaxf(m, ms[j]);
   m = block_reduce(m, true);
   float l = 0.f;
-  for (int s = tid; s < S; s += T) {
-    const float ms = w[s * (D + 4)];
-    const float a = (ms == -INFINITY) ? 0.f : exp2f(ms - m);   // maxima in base-2 units
-    weight[s] = a;
-    l += a * w[s * (D + 4) + 1];
+#pragma unroll
+  for (int j = 0; j < kSplitsPerThread; ++j) {
+    const int s = tid + T * j;
+    if (s < S) {
+      const float a = (ms[j] == -INFINITY) ? 0.f : exp2f(ms[j] - m);   // maxima in base-2 units
+      weight[s] = a;
+      l += a * ls[j];
+    }
   }
   l = block_reduce(l, false);   // its barriers also publish weight[]
   float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int s = g + G * j;
+    if (s < S) acc += weight[s] * opre[j];
+  }
 #pragma unroll 8
-  for (int s = g; s < S; s += G) acc += weight[s] * w[s * (D + 4) + 4 + d];
+  for (int s = g + G * kPre; s < S; s += G) acc += weight[s] * w[s * (D + 4) + 4 + d];
   if (g > 0) gsum[g - 1][d] = acc;
   __syncthreads();
   if (g == 0) {

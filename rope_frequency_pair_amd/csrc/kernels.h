@@ -59,7 +59,8 @@ struct DecodeParams {
   float* ws;                             // [batch, q_len, h_q, splits, head_dim + 4]
   int64_t qs[3], ks[3], vs[3], os[3];   // q / o: (batch, head, token) element strides
   int32_t batch, h_q, h_kv, splits;
-  int32_t causal, group, q_len, pad1;   // group = query heads per kv head; q_len tokens per sequence
+  int32_t causal, group, q_len;         // group = query heads per kv head; q_len tokens per sequence
+  int32_t heads_in_order;               // 1: kv head k serves query heads k * group + 0 .. group - 1
   // Block-sparse key selection (nullptr: every key): bit kb % 32 of word
   // kb / 32 of row (b * h_kv + kvh), rows of sel_words words: the sequence's
   // kv head attends key block kb (64 keys).
