@@ -7,7 +7,7 @@ import torch
 import oracle
 import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import synth
-from tests.gpu_util import BF16_TOL, check_rows, max_err, say, sync, to_np
+from tests.gpu_util import BF16_TOL, bf16_err, check_rows, max_err, say, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def _check(q, kc, vc, kv_len, q_pos, base, k_turns, splits, causal=True, window_
                         [kv_len[b] for b in batches], [q_pos[b] for b in batches], base, k_turns,
                         causal=causal, window_on=window_on, heads=heads, kv_head_of_q=kv_head_of_q)
     got = to_np(out[batches][:, heads])
-    err = max_err(got, ref)
+    err = bf16_err(got, ref)
     say(f"  splits={splits} max abs err {err:.3e}")
     assert np.isfinite(got).all()
     assert err <= BF16_TOL
@@ -132,7 +132,7 @@ def test_decode_banded_ragged_batch(d, splits):
                             num_splits=splits)
     sync()
     ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.5)
-    err = max_err(to_np(got), ref)
+    err = bf16_err(to_np(got), ref)
     say(f"  banded max abs err {err:.3e}")
     assert err <= BF16_TOL
     rows = atw.decode(q, kc, vc, kv_len, q_pos, rope_base=1e4, k_turns=0.5, window_on=False,
@@ -154,7 +154,7 @@ def test_decode_banded_non_causal_window_off_head_map():
         sync()
         ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), [500], [qp], 1e4, 0.5, causal=causal,
                             window_on=window_on, kv_head_of_q=hm)
-        err = max_err(to_np(got), ref)
+        err = bf16_err(to_np(got), ref)
         say(f"  causal={causal} window_on={window_on} max abs err {err:.3e}")
         assert err <= BF16_TOL
 

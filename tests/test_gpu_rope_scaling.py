@@ -13,7 +13,7 @@ import torch
 import oracle
 import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import synth
-from tests.gpu_util import BF16_TOL, F32_TOL, max_err, say, sync, to_np
+from tests.gpu_util import BF16_TOL, bf16_err, F32_TOL, max_err, say, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_prefill_bf16_rope_scaling(d, name):
         out = atw.prefill(q, k, v, rope_base=1e4, k_turns=k_turns, rope_scaling=sc)
         sync()
         ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, k_turns, scaling=sc)
-        err = max_err(to_np(out), ref)
+        err = bf16_err(to_np(out), ref)
         say(f"  k={k_turns} max abs err {err:.3e}")
         assert np.isfinite(to_np(out)).all() and err <= BF16_TOL
 
@@ -78,7 +78,7 @@ def test_decode_rope_scaling(banded, d):
                          rope_scaling=SMALL_LLAMA3)
     sync()
     ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.6, scaling=SMALL_LLAMA3)
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert err <= BF16_TOL
 
@@ -105,7 +105,7 @@ def test_prefill_bf16_explicit_widths(d, rule):
     out = atw.prefill(q, k, v, rope_base=1e4, k_turns=0.0, rope_scaling=sc)
     sync()
     ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, 0.0, scaling=sc)
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert np.isfinite(to_np(out)).all() and err <= BF16_TOL
 
@@ -137,7 +137,7 @@ def test_decode_explicit_widths(banded):
                          rope_scaling=sc)
     sync()
     ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.0, scaling=sc)
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert err <= BF16_TOL
 
@@ -152,7 +152,7 @@ def test_prefill_sparse_explicit_widths():
                              rope_scaling=sc)
     sync()
     ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, 0.0, scaling=sc, key_blocks=sel.numpy())
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert np.isfinite(to_np(out)).all() and err <= BF16_TOL
 
@@ -172,6 +172,6 @@ def test_decode_multi_explicit_widths(banded):
                            k_banded=banded, rope_scaling=sc)
     sync()
     ref = oracle.decode_multi(to_np(q), to_np(kc), to_np(vc), kv_len, q_pos, 1e4, 0.0, scaling=sc)
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert np.isfinite(to_np(out)).all() and err <= BF16_TOL

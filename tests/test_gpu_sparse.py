@@ -15,7 +15,7 @@ import torch
 import oracle
 import rope_frequency_pair_amd as atw
 from rope_frequency_pair_amd import synth
-from tests.gpu_util import BF16_TOL, check_rows, max_err, sample_rows, say, sync, to_np
+from tests.gpu_util import BF16_TOL, bf16_err, check_rows, max_err, sample_rows, say, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_sparse_prefill_parity(d, h_q, h_kv, n_q, n_kv, q_pos0, causal, k_turns,
         sync()
         ref = oracle.prefill(*ref_args, causal=causal, window_on=window_on, key_blocks=sel.numpy())
         got = to_np(out)
-        err = max_err(got, ref)
+        err = bf16_err(got, ref)
         say(f"  window_on={window_on} max abs err {err:.3e}")
         assert np.isfinite(got).all() and err <= BF16_TOL
         # a query block that attends nothing gives exactly 0
@@ -82,7 +82,7 @@ def test_sparse_prefill_rope_scaling():
     sync()
     ref = oracle.prefill(to_np(q), to_np(k), to_np(v), 0, 1e4, 0.6, scaling=SMALL_LLAMA3,
                          key_blocks=sel.numpy())
-    err = max_err(to_np(out), ref)
+    err = bf16_err(to_np(out), ref)
     say(f"  max abs err {err:.3e}")
     assert err <= BF16_TOL
 
@@ -135,7 +135,7 @@ def test_sparse_decode_parity(d, banded, splits):
         ref = oracle.decode(to_np(q), to_np(kc), to_np(vc), kv_len, [n - 1 for n in kv_len], 1e4, k_turns,
                             window_on=window_on, key_blocks=sel.numpy())
         got = to_np(out)
-        err = max_err(got, ref)
+        err = bf16_err(got, ref)
         say(f"  window_on={window_on} k={k_turns} max abs err {err:.3e}")
         assert np.isfinite(got).all() and err <= BF16_TOL
         assert np.all(got[1, 4:] == 0.0)
