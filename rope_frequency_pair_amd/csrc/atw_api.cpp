@@ -552,8 +552,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   // kv head kv serves query heads kv * group .. kv * group + group - 1, in
   // order: the kernels then compute a column's query head instead of reading
   // it from the tables
-  p.heads_in_order = 1;
-  for (int i = 0; i < h_q; ++i)
+  p.heads_in_order = h_q % h_kv == 0 ? 1 : 0;   // (an explicit map may give h_q < h_kv)
+  for (int i = 0; i < h_q && p.heads_in_order; ++i)
     if (p.qh_of_kv[i] != i || kvh[i] != i / p.group) p.heads_in_order = 0;
   if (sparse) {
     p.sel = block_mask;

@@ -55,6 +55,19 @@ def test_decode_non_causal_and_head_map():
     _check(q, kc, vc, [500], [200], 1e4, 0.5, 5, causal=False, kv_head_of_q=[2, 2, 0, 1, 0, 1])
 
 
+def test_decode_fewer_query_heads_than_kv_heads():
+    """An explicit head map may leave kv heads unread (2 query heads over 4
+    kv heads): those kv heads' waves have no columns, and the query heads
+    still read their own kv heads -- also with the heads in model order of a
+    default-looking prefix (query head 0 -> kv head 0)."""
+    say("decode h_q < h_kv with a head map")
+    q, kc, vc = synth.decode_inputs(2, 2, 4, 300, 128, torch.bfloat16, 24, device="cuda")
+    for hmap in ([3, 1], [0, 2], [0, 1]):
+        _check(q, kc, vc, [300, 211], [299, 210], 1e4, 0.5, 3, kv_head_of_q=hmap)
+    q, kc, vc = synth.decode_inputs(1, 6, 3, 300, 64, torch.bfloat16, 25, device="cuda")
+    _check(q, kc, vc, [300], [299], 1e4, 0.5, 4, kv_head_of_q=[0, 0, 1, 1, 2, 2])   # in order, given
+
+
 def test_decode_row_equals_prefill_row():
     """A decode step at position n against keys 0..n equals prefill row n."""
     say("decode row == prefill row")
