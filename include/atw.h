@@ -39,8 +39,9 @@
  *   - window_on = 0 is the plain causal RoPE attention path (k is ignored);
  *     k = +inf with window_on = 1 gives the same result.
  *   - Supported on the GPU: head_dim 64 or 128; dtype ATW_BF16 (bf16 in and
- *     out, fp32 accumulation, bf16 MFMA) for prefill and decode, ATW_F32
- *     (fp32 in and out, fp32 MFMA) for prefill.  Positions must be < 2^30.
+ *     out, fp32 accumulation, fp16 matrix-core operands) or ATW_BF16_F32OUT
+ *     (the same with an fp32 output) for prefill and decode, ATW_F32 (fp32
+ *     in and out, fp32 MFMA) for prefill.  Positions must be < 2^30.
  */
 #ifndef ATW_H
 #define ATW_H
@@ -62,6 +63,10 @@ extern "C" {
 /* element types */
 #define ATW_F32 0
 #define ATW_BF16 1
+/* bf16 inputs with an fp32 output (o holds floats; o_strides count floats):
+ * the same computation as ATW_BF16 without the final rounding of the output
+ * to bf16.  Accepted by the bf16 prefill and decode entry points. */
+#define ATW_BF16_F32OUT 2
 
 /* Largest integer window; returned for every pair when the window is off or
  * k = +inf (2^62). */
@@ -217,7 +222,8 @@ int atw_decode_sparse(const void* q, const void* k_cache, const void* v_cache, v
  *     per-chunk maxima that choose those scales; ATW_F32: none needed, may
  *     be NULL).  Contents on entry are ignored; overwritten by the call.
  *   ATW_BF16 arithmetic: matrix-core operands fp16 (rotated queries and keys,
- *     values, softmax weights), accumulation fp32, output bf16.
+ *     values, softmax weights), accumulation fp32, output bf16
+ *     (ATW_BF16_F32OUT: fp32).
  * Requires n_q >= 0, n_kv >= 1, q_pos0 >= 0, h_q % h_kv == 0 without a map,
  * rope_base > 1, k_turns > 0 when window_on, batch <= 65535.  n_q = 0
  * launches nothing.
@@ -305,7 +311,8 @@ size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, i
  *   workspace: device buffer of at least atw_decode_workspace_bytes(...)
  *           bytes for the per-split partial results (max, sum, unnormalised
  *           output); contents on entry are ignored.
- * batch <= 256; at most 16 query heads per kv head.  dtype must be ATW_BF16.
+ * batch <= 256; at most 16 query heads per kv head.  dtype ATW_BF16 or
+ * ATW_BF16_F32OUT.
  */
 int atw_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int32_t dtype,
                int64_t batch, const int64_t* kv_len, const int64_t* q_pos,

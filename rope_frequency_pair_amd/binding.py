@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libatw.so")
 
 ATW_OK, ATW_EINVAL, ATW_EUNSUPPORTED, ATW_EWORKSPACE, ATW_EHIP = 0, -1, -2, -3, -4
-ATW_F32, ATW_BF16 = 0, 1
+ATW_F32, ATW_BF16, ATW_BF16_F32OUT = 0, 1, 2
 UNBOUNDED = 1 << 62
 
 EXPORTED = [
@@ -206,6 +206,17 @@ def _dtype_code(t):
     raise AtwError(ATW_EUNSUPPORTED, f"unsupported dtype {t.dtype}")
 
 
+def _io_code(q, out):
+    """Element-type code of a call: the inputs' type, or ATW_BF16_F32OUT for
+    bf16 inputs written to an fp32 output tensor."""
+    import torch
+    if q.dtype == torch.bfloat16 and out.dtype == torch.float32:
+        return ATW_BF16_F32OUT
+    if out.dtype != q.dtype:
+        raise AtwError(ATW_EUNSUPPORTED, f"output dtype {out.dtype} with inputs of dtype {q.dtype}")
+    return _dtype_code(q)
+
+
 def _head_map(kv_head_of_q):
     if kv_head_of_q is None:
         return None
@@ -351,7 +362,7 @@ def prefill(q, k, v, *, rope_base, k_turns, q_pos0=0, causal=True, window_on=Tru
         entry, rope_arg = lib.atw_prefill_rope, ctypes.byref(rdesc)
     _check(entry(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-        ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
+        ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
         _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
         _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), rope_arg, float(k_turns),
         int(causal), int(window_on), float(scale or 0.0), ws_ptr, ws_len, _stream_ptr(stream)))
@@ -385,7 +396,7 @@ def prefill_sparse(q, k, v, block_mask, *, rope_base, k_turns, q_pos0=0, causal=
     rdesc = rope_descriptor(rope_base, rope_scaling, D)
     _check(lib.atw_prefill_sparse(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-        ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
+        ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B, Nq, Nkv, int(q_pos0), Hq, Hkv,
         _head_map(kv_head_of_q), D, _arr64(q.stride()[:3]), _arr64(k.stride()[:3]),
         _arr64(v.stride()[:3]), _arr64(out.stride()[:3]), ctypes.byref(rdesc), float(k_turns),
         int(causal), int(window_on), float(scale or 0.0), ctypes.c_void_p(block_mask.data_ptr()),
@@ -462,7 +473,7 @@ def _decode(entry, q, k_cache, v_cache, kv_len, q_pos, rope_base, k_turns, causa
         entry, rope_arg = entry + "_rope", ctypes.byref(rdesc)
     _check(getattr(lib, entry)(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
-        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
         _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
         _arr64(out.stride()[:2]), rope_arg, float(k_turns), int(causal), int(window_on),
@@ -485,7 +496,7 @@ def decode_noalloc(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, ca
     q_pos = [int(x) for x in (q_pos if hasattr(q_pos, "__len__") else [q_pos] * B)]
     _check(lib.atw_decode_noalloc(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
-        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
         _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
         _arr64(out.stride()[:2]), float(rope_base), float(k_turns), int(causal), int(window_on),
@@ -522,7 +533,7 @@ def decode_sparse(q, k_cache, v_cache, kv_len, q_pos, block_mask, *, rope_base, 
     rdesc = rope_descriptor(rope_base, rope_scaling, D)
     _check(lib.atw_decode_sparse(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
-        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B,
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D,
         _arr64(q.stride()[:2]), _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]),
         _arr64(out.stride()[:2]), ctypes.byref(rdesc), float(k_turns), int(causal), int(window_on),
@@ -555,7 +566,7 @@ def decode_multi(q, k_cache, v_cache, kv_len, q_pos, *, rope_base, k_turns, wind
     os_ = (out.stride(0), out.stride(2), out.stride(1))
     _check(lib.atw_decode_multi(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
-        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _dtype_code(q), B, T,
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(out.data_ptr()), _io_code(q, out), B, T,
         _arr64(kv_len), _arr64(q_pos), Hq, Hkv, _head_map(kv_head_of_q), D, _arr64(qs),
         _arr64(k_cache.stride()[:3]), _arr64(v_cache.stride()[:3]), _arr64(os_), int(bool(k_banded)),
         ctypes.byref(rdesc), float(k_turns), int(window_on), float(scale or 0.0), int(num_splits),

@@ -273,6 +273,9 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
                  const uint32_t* block_mask = nullptr, bool sparse = false) {
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "prefill supports head_dim 64 and 128 (got %d)", head_dim);
+  // bf16 inputs with an fp32 output: the bf16 path, storing floats
+  const bool out_f32 = dtype == ATW_BF16_F32OUT;
+  if (out_f32) dtype = ATW_BF16;
   if (sparse) {
     if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "block-sparse prefill supports dtype ATW_BF16 only");
     if (block_mask == nullptr && n_q > 0) return fail(ATW_EINVAL, "block_mask is NULL");
@@ -294,7 +297,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   if (int e = check_strides("q", q_strides, 3, elem)) return e;
   if (int e = check_strides("k", k_strides, 3, elem)) return e;
   if (int e = check_strides("v", v_strides, 3, elem)) return e;
-  if (int e = check_strides("o", o_strides, 3, elem)) return e;
+  if (int e = check_strides("o", o_strides, 3, out_f32 ? 4 : elem)) return e;
   const int64_t rows = dtype == ATW_BF16 ? atw::prefill_bf16_block_rows(head_dim) : atw::kPrefillBlockRows;
   const int64_t n_qblk = (n_q + rows - 1) / rows;
   if (n_qblk * h_q * batch >= (int64_t(1) << 31)) return fail(ATW_EUNSUPPORTED, "grid too large");
@@ -323,6 +326,7 @@ int prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t d
   p.causal = causal != 0;
   p.n_qblk = (int32_t)n_qblk;
   p.n_kv_heads = h_kv;
+  p.out_f32 = out_f32 ? 1 : 0;
   const double scale = softmax_scale > 0 ? softmax_scale : 1.0 / std::sqrt((double)head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
   // query heads grouped by kv head: workgroups of one kv head share an XCD
@@ -441,7 +445,9 @@ int atw_pruned_terms_sparse(int64_t n_q, int64_t n_kv, int64_t q_pos0, int32_t h
 
 size_t atw_prefill_workspace_bytes(int32_t dtype, int64_t batch, int32_t h_kv, int64_t n_kv,
                                    int32_t head_dim) {
-  if (dtype != ATW_BF16 || batch <= 0 || h_kv <= 0 || n_kv <= 0 || head_dim <= 0) return 0;
+  if ((dtype != ATW_BF16 && dtype != ATW_BF16_F32OUT) || batch <= 0 || h_kv <= 0 || n_kv <= 0 ||
+      head_dim <= 0)
+    return 0;
   return atw::prefill_pack_bytes(batch, h_kv, n_kv, head_dim);
 }
 
@@ -464,7 +470,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
                 int64_t mask_words = 0, bool sparse = false) {
   if (head_dim != 64 && head_dim != 128)
     return fail(ATW_EUNSUPPORTED, "decode supports head_dim 64 and 128 (got %d)", head_dim);
-  if (dtype != ATW_BF16) return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 only");
+  if (dtype != ATW_BF16 && dtype != ATW_BF16_F32OUT)
+    return fail(ATW_EUNSUPPORTED, "decode supports dtype ATW_BF16 and ATW_BF16_F32OUT only");
+  const bool out_f32 = dtype == ATW_BF16_F32OUT;
   if (batch <= 0 || batch > atw::kMaxDecodeBatch)
     return fail(ATW_EUNSUPPORTED, "batch must be in 1..%d", atw::kMaxDecodeBatch);
   if (num_splits <= 0 || num_splits > atw::kMaxDecodeSplits)
@@ -511,6 +519,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   p.k = k_cache;
   p.v = v_cache;
   p.o = o;
+  p.out_f32 = out_f32 ? 1 : 0;
   p.ws = static_cast<float*>(workspace);
   p.qs[0] = q_strides[0];
   p.qs[1] = q_strides[1];
@@ -722,7 +731,7 @@ int atw_decode_multi(const void* q, const void* k_cache, const void* v_cache, vo
       kvl[bb] = kv_len[bb] < pos[bb] + n ? kv_len[bb] : pos[bb] + n;
     }
     const void* qg = static_cast<const char*>(q) + (int64_t)t0 * q_strides[2] * 2;
-    void* og = static_cast<char*>(o) + (int64_t)t0 * o_strides[2] * 2;
+    void* og = static_cast<char*>(o) + (int64_t)t0 * o_strides[2] * (dtype == ATW_BF16_F32OUT ? 4 : 2);
     if (int e = decode_impl(qg, k_cache, v_cache, og, dtype, batch, n, q_strides[2], o_strides[2], kvl,
                             pos, h_q, h_kv, kv_head_of_q, head_dim, q_strides, k_strides, v_strides,
                             o_strides, rw, 1, window_on, softmax_scale, num_splits,

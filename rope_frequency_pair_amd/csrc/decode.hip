@@ -881,8 +881,12 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   if (g == 0) {
 #pragma unroll
     for (int i = 0; i < G - 1; ++i) acc += gsum[i][d];
-    __bf16* o = (__bf16*)p.o + b * p.os[0] + qh * p.os[1] + tok * p.os[2];
-    o[d] = (__bf16)(l > 0.f ? acc / l : 0.f);   // no attended key: 0
+    const float res = l > 0.f ? acc / l : 0.f;   // no attended key: 0
+    const int64_t at = b * p.os[0] + qh * p.os[1] + tok * p.os[2] + d;
+    if (p.out_f32)
+      ((float*)p.o)[at] = res;
+    else
+      ((__bf16*)p.o)[at] = (__bf16)res;
   }
 }
 

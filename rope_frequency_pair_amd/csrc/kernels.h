@@ -35,6 +35,7 @@ struct PrefillParams {
   int32_t batch, n_q, n_kv, q_pos0;
   int32_t h_q, causal, n_qblk, n_kv_heads;
   int32_t n_kt;                          // packed key tiles per (batch, kv head)
+  int32_t out_f32;                       // bf16: 1 = fp32 output (o is float)
   float scale_log2;                      // softmax scale * log2(e)
   // Block-sparse key selection (nullptr: every key).  Bit kb % 32 of word
   // kb / 32 of row ((b * h_q + hq) * n_sel_qb + qb), rows of sel_words words:
@@ -65,7 +66,8 @@ struct DecodeParams {
   // kb / 32 of row (b * h_kv + kvh), rows of sel_words words: the sequence's
   // kv head attends key block kb (64 keys).
   const uint32_t* sel;
-  int32_t sel_words, pad2;
+  int32_t sel_words;
+  int32_t out_f32;                       // 1 = fp32 output (o is float)
   float scale_log2;
   int32_t kv_len[kMaxDecodeBatch];
   int32_t q_pos[kMaxDecodeBatch];

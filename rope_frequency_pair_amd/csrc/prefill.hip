@@ -291,7 +291,7 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   }
 
   const __bf16* qbase = (const __bf16*)p.q + bb * p.qs[0] + hq * p.qs[1];
-  __bf16* obase = (__bf16*)p.o + bb * p.os[0] + hq * p.os[1];
+  const int64_t obase = bb * p.os[0] + hq * p.os[1];   // element offset of the output head
   const int64_t tix0 = ((int64_t)bb * p.n_kv_heads + kvh) * p.n_kt;
   const uint16_t* kpk = (const uint16_t*)p.kp + tix0 * TILE;
   const uint16_t* vpk = (const uint16_t*)p.vp + tix0 * TILE;
@@ -720,16 +720,22 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   const float inv = l_tot > 0.f ? __builtin_amdgcn_ldexpf(1.f / l_tot, ev) : 0.f;
   const int row = w_first + l32;
   if (wave_rows && row <= w_last) {
-    __bf16* orow = obase + (int64_t)row * p.os[2];
+    const int64_t orow = obase + (int64_t)row * p.os[2];
 #pragma unroll
     for (int b = 0; b < C::ND; ++b)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * b + 8 * v4 + 4 * sh;
-        u32x2 w;
-        w[0] = pack_bf16(oacc[b][4 * v4] * inv, oacc[b][4 * v4 + 1] * inv);
-        w[1] = pack_bf16(oacc[b][4 * v4 + 2] * inv, oacc[b][4 * v4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+        const float o0 = oacc[b][4 * v4] * inv, o1 = oacc[b][4 * v4 + 1] * inv;
+        const float o2 = oacc[b][4 * v4 + 2] * inv, o3 = oacc[b][4 * v4 + 3] * inv;
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4*>((float*)p.o + orow + d0) = f32x4{o0, o1, o2, o3};
+        } else {
+          u32x2 w;
+          w[0] = pack_bf16(o0, o1);
+          w[1] = pack_bf16(o2, o3);
+          *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d0) = w;
+        }
       }
   }
 }

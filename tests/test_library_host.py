@@ -150,6 +150,7 @@ def test_invalid_arguments(lib):
     need = lib.atw_prefill_workspace_bytes(1, 1, 2, 10, 128)
     assert need == 2 * 1 * 2 * 1 * 64 * 128 * 2 + 1 * 2 * 32 * 2 * 4
     assert lib.atw_prefill_workspace_bytes(0, 1, 2, 10, 128) == 0
+    assert lib.atw_prefill_workspace_bytes(atw.binding.ATW_BF16_F32OUT, 1, 2, 10, 128) == need
     assert pre(ws=need - 1) == atw.binding.ATW_EWORKSPACE
 
 
@@ -169,6 +170,10 @@ def test_decode_invalid_arguments(lib):
     assert dec(kv=binding._arr64([0])) == atw.binding.ATW_EINVAL
     assert dec(splits=0) == atw.binding.ATW_EINVAL
     assert dec(dtype=0) == atw.binding.ATW_EUNSUPPORTED
+    assert dec(dtype=3) == atw.binding.ATW_EUNSUPPORTED
+    # bf16 inputs with an fp32 output validate like bf16 (the workspace check
+    # is reached)
+    assert dec(dtype=atw.binding.ATW_BF16_F32OUT, ws=need - 1) == atw.binding.ATW_EWORKSPACE
     # the banded entry point validates the same way
     assert lib.atw_decode_banded(fake, fake, fake, fake, 1, 1, kv, qp, 4, 2, None, 128, s2, s3, s3,
                                  s2, 1e4, 4.0, 1, 1, 0.0, 8, fake, need - 1,
