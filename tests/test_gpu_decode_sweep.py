@@ -23,7 +23,7 @@ def _case(seed):
     r = np.random.default_rng(seed)
     d = int(r.choice([64, 128]))
     h_kv = int(r.integers(1, 3))
-    g = int(r.choice([1, 2, 4, 7]))
+    g = int(r.choice([1, 2, 4, 7, 16]))
     T = 1 if r.random() < 0.5 else int(r.integers(2, 5))
     while g * T > 16:
         T -= 1
