@@ -33,7 +33,7 @@
 //    resident on one XCD (workgroup i runs on XCD i mod 8) are consecutive
 //    blocks of one (batch, kv head), so they share K'/V tiles in its L2;
 //  * scores are computed transposed, S^T = K' Q'^T, with
-//    v_mfma_f32_32x32x16_bf16, so each lane holds 16 keys of one query
+//    v_mfma_f32_32x32x16_f16, so each lane holds 16 keys of one query
 //    column and the row max / sum are mostly in-lane; lanes l and l+32 share
 //    a query;
 //  * the contraction axis is ordered pair by pair ((r, r+h) adjacent): one
