@@ -476,6 +476,31 @@ def main():
         del q1, k1, v1, o1
         torch.cuda.empty_cache()
 
+        # Qwen2.5-7B-1M shape (28 / 4 heads, d = 128, base 1e7, k = 8): one
+        # causal prefill call of 256K and of 512K tokens, window ON vs OFF
+        wl7 = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
+        longp = {}
+        for n in (262144, 524288):
+            log(f"[bench] Qwen2.5-7B-1M-shaped prefill, {n} tokens")
+            ql, kl, vl = synth.prefill_inputs(1, wl7.h_q, wl7.h_kv, n, n, wl7.head_dim, torch.bfloat16,
+                                              wl7.seed + 7, device=dev)
+            ol = torch.empty_like(ql)
+            step(True, ql, kl, vl, ol, wl7)
+            step(False, ql, kl, vl, ol, wl7)
+            a, b = [], []
+            for _ in range(3):
+                a += time_launches(lambda: step(True, ql, kl, vl, ol, wl7), stream, 1)
+                b += time_launches(lambda: step(False, ql, kl, vl, ol, wl7), stream, 1)
+            fo, fd, sh = prefill_flops(atw, n, wl7.head_dim, wl7.h_q, 1, wl7.rope_base, wl7.k_turns, True)
+            longp[str(n)] = {"ms_on": round(statistics.median(a), 2), "ms_off": round(statistics.median(b), 2),
+                             "on_off_speedup": round(statistics.median(b) / statistics.median(a), 3),
+                             "tflops_algorithmic_on": round(fo / (statistics.median(a) * 1e-3) / 1e12, 1),
+                             "tflops_dense_equiv_on": round(fd / (statistics.median(a) * 1e-3) / 1e12, 1),
+                             "pruned_share": round(sh, 4), "ceiling_2_over_1_plus_s": round(2.0 / (2.0 - sh), 3)}
+            del ql, kl, vl, ol
+            torch.cuda.empty_cache()
+        result["prefill_qwen7b_1m_shape_long"] = longp
+
         # split-KV decode, Qwen2.5-7B-1M shape, 512K cache, 8 sequences, 64 splits
         wd = synth.WORKLOADS["qwen2.5-7b-1m-decode-512k"]
         log(f"[bench] {wd.name}")
