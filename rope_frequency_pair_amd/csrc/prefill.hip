@@ -542,6 +542,11 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
       // only for its own reads.  (r_full == H, every pair partial or pruned:
       // k-step NKS-1 with all its slots masked, which yields -r; its K' slot
       // holds finite data, as the K' buffers start zeroed)
+      // The waves of a SIMD leave the barrier together and all start with
+      // their QK^T MFMAs: the wave issuing them (and then its late copies)
+      // takes precedence over the others' vector work until they are issued
+      // (measured 0.5-1.9% faster than equal priority, same output).
+      __builtin_amdgcn_s_setprio(1);
       const int kk0 = min(r_full >> 3, C::NKS - 1);
       {
         // (head_dim 64: no early reads, its register budget is 128)
@@ -637,6 +642,7 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
         sacc[1] += x[1];
       }
       if (t_next >= 0) dma(t_next, slot ^ 1, !kEarlyV, !kEarlyK);
+      __builtin_amdgcn_s_setprio(0);
       copied = true;
       // the query operand's power of two (only for queries reaching 2^14)
       if (eq != 0) {
