@@ -81,12 +81,6 @@ namespace {
 constexpr int kRowsW = 32;
 constexpr int kTK = kPrefillTileK;
 constexpr float kRefLag = 6.0f;       // reference r = running max - 6 (base 2)
-// Which copies of the next tile are issued at the top of a tile (the rest
-// after the QK^T MFMAs): head_dim 64 issues all late (its QK^T is short;
-// measured 4-5% faster at 32K), head_dim 128 all early (splitting the copies
-// or issuing either part late measured no faster or slower).
-template <int D> constexpr bool kCopyEarlyV = D == 128;
-template <int D> constexpr bool kCopyEarlyK = D == 128;
 constexpr float kRaise = 14.0f;       // raise r when a score passes it by more
 
 // Power-of-two scales of one (batch, kv head): the range pass's chunk maxima
@@ -383,30 +377,26 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
     return first_kstep(w_lane, dmin);
   };
   typedef __attribute__((address_space(3))) void lds_void;
-  // copies of tile t into LDS slot `slot`: the V blocks and/or the K' blocks
-  auto dma = [&](int t, int slot, bool do_v, bool do_k) {
+  // copies of tile t into LDS slot `slot`: this wave's V blocks and K' blocks
+  auto dma = [&](int t, int slot) {
     const uint16_t* ks = kpk + (int64_t)t * TILE;
     const uint16_t* vs = vpk + (int64_t)t * TILE;
     uint16_t* kd = &lk[slot][0];
     uint16_t* vd = &lv[slot][0];
-    if (do_v) {
 #pragma unroll
-      for (int i = 0; i < C::VPW; ++i) {
-        const int blk = wave + C::WAVES * i;
-        if (C::VBLK % C::WAVES == 0 || blk < C::VBLK)
-          __builtin_amdgcn_global_load_lds((const void*)(vs + blk_off(blk, lane)),
-                                           (lds_void*)(vd + blk_off(blk, 0)), 16, 0, 0);
-      }
+    for (int i = 0; i < C::VPW; ++i) {
+      const int blk = wave + C::WAVES * i;
+      if (C::VBLK % C::WAVES == 0 || blk < C::VBLK)
+        __builtin_amdgcn_global_load_lds((const void*)(vs + blk_off(blk, lane)),
+                                         (lds_void*)(vd + blk_off(blk, 0)), 16, 0, 0);
     }
-    if (do_k) {
-      const int ks0 = stage_ks(t);
+    const int ks0 = stage_ks(t);
 #pragma unroll
-      for (int i = 0; i < C::KPW; ++i) {
-        const int blk = wave + C::WAVES * i;
-        if ((C::KBLK % C::WAVES == 0 || blk < C::KBLK) && (blk >> 1) >= ks0)
-          __builtin_amdgcn_global_load_lds((const void*)(ks + blk_off(blk, lane)),
-                                           (lds_void*)(kd + blk_off(blk, 0)), 16, 0, 0);
-      }
+    for (int i = 0; i < C::KPW; ++i) {
+      const int blk = wave + C::WAVES * i;
+      if ((C::KBLK % C::WAVES == 0 || blk < C::KBLK) && (blk >> 1) >= ks0)
+        __builtin_amdgcn_global_load_lds((const void*)(ks + blk_off(blk, lane)),
+                                         (lds_void*)(kd + blk_off(blk, 0)), 16, 0, 0);
     }
   };
 
@@ -468,17 +458,17 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
   int t = -1, t_next = -1, slot = 0;
   bool own = false, own_next = false;
   next_tile(&t, &own);
-  if (t >= 0) dma(t, 0, true, true);
+  if (t >= 0) dma(t, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   while (t >= 0) {
     next_tile(&t_next, &own_next);
-    // copies of the next tile: the early part at the top of the tile, the
-    // rest after the QK^T MFMAs are issued (kCopyEarlyV / kCopyEarlyK)
-    constexpr bool kEarlyV = kCopyEarlyV<D>, kEarlyK = kCopyEarlyK<D>;
-    bool copied = false;
-    if ((kEarlyV || kEarlyK) && t_next >= 0) dma(t_next, slot ^ 1, kEarlyV, kEarlyK);
+    // copies of the next tile, issued at the top of the tile by every wave
+    // (whether it works this tile or not).  Issued after the QK^T MFMAs
+    // instead, they measured 2.5% slower at head_dim 128 and 0.5-1.8% slower
+    // at head_dim 64; split between the two places, no faster.
+    if (t_next >= 0) dma(t_next, slot ^ 1);
 
     const int m_lo = t * kTK;
     const int m_hi = min(m_lo + kTK - 1, n_kv - 1);
@@ -543,9 +533,9 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
       // k-step NKS-1 with all its slots masked, which yields -r; its K' slot
       // holds finite data, as the K' buffers start zeroed)
       // The waves of a SIMD leave the barrier together and all start with
-      // their QK^T MFMAs: the wave issuing them (and then its late copies)
-      // takes precedence over the others' vector work until they are issued
-      // (measured 0.5-1.9% faster than equal priority, same output).
+      // their QK^T MFMAs: the wave issuing them takes precedence over the
+      // others' vector work until they are issued (measured 0.5-1.9% faster
+      // than equal priority, same output).
       __builtin_amdgcn_s_setprio(1);
       const int kk0 = min(r_full >> 3, C::NKS - 1);
       {
@@ -641,9 +631,7 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
         sacc[0] += x[0];
         sacc[1] += x[1];
       }
-      if (t_next >= 0) dma(t_next, slot ^ 1, !kEarlyV, !kEarlyK);
       __builtin_amdgcn_s_setprio(0);
-      copied = true;
       // the query operand's power of two (only for queries reaching 2^14)
       if (eq != 0) {
         sacc[0] *= score_unscale;
@@ -712,7 +700,6 @@ __global__ __launch_bounds__(PCfg<D>::THREADS, D == 64 ? 4 : 3) void prefill_bf1
       l_run += lsum;
     }
 
-    if (!copied && t_next >= 0) dma(t_next, slot ^ 1, !kEarlyV, !kEarlyK);   // a tile this wave did not work
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next tile have landed
     __syncthreads();
     t = t_next;
